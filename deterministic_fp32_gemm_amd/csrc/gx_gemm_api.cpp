@@ -1,0 +1,431 @@
+// Host entry points of libsdm_gx_gemm: argument checks, the launch planner, single-step, multi-step and prepared
+// launches. Everything that decides whether and how to launch runs here; every arithmetic step of the update runs
+// in the kernels of gx_gemm_kernel.hip.
+//
+// The checks follow the page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py": the host entry
+// gx_gemm (shape, step range, overlap and alignment checks) and supported(); the prepared launch follows its
+// per-backward plan (gx_gemm_plan / gx_gemm_plan_launch: validate once at ti_max, then patch only ti).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/sdm_gx_gemm.h"
+#include "gx_gemm_kernel.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = static_cast<int>(e);
+    return SDM_GX_ERR_HIP;
+}
+
+constexpr uint64_t kLaunchMagic = 0x314843554E4C4753ull;   // prepared-launch tag
+
+// ---- argument checks (no device access) ---------------------------------------------------------------------------
+int64_t row_extent(int64_t N, int64_t C, int64_t ld, int64_t hd) {   // elements reachable in a [N][C] ld-strided array
+    return (N * C - 1) * ld + hd;
+}
+
+bool overlaps(const void* a, int64_t a_elems, const void* b, int64_t b_elems) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t a1 = a0 + static_cast<uintptr_t>(a_elems) * sizeof(float);
+    const uintptr_t b1 = b0 + static_cast<uintptr_t>(b_elems) * sizeof(float);
+    return a0 < b1 && b0 < a1;
+}
+
+int check_args(const float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv, int64_t N, int64_t ti,
+               int64_t P, int64_t C, int64_t hd) {
+    if (!du || !x || !dv) return SDM_GX_ERR_NULL;
+    if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT) return SDM_GX_ERR_SHAPE;
+    if (N < 1 || N >= SDM_GX_N_LIMIT || P < 1) return SDM_GX_ERR_SHAPE;
+    if (ld_u < hd || ld_dv < hd || ld_u >= SDM_GX_LD_LIMIT || ld_dv >= SDM_GX_LD_LIMIT) return SDM_GX_ERR_STRIDE;
+    // bounds by division before any product (no overflow for any int64 ti / P)
+    if (P > N || ti < 0 || ti >= N / P) return SDM_GX_ERR_STEP;
+    if ((reinterpret_cast<uintptr_t>(du) | reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dv)) & 3u)
+        return SDM_GX_ERR_ALIGN;
+    const int64_t nu = row_extent(N, C, ld_u, hd), nv = row_extent(N, C, ld_dv, hd), nx = N * C * C;
+    if (overlaps(du, nu, x, nx) || overlaps(du, nu, dv, nv)) return SDM_GX_ERR_OVERLAP;
+    return SDM_GX_OK;
+}
+
+// ---- device facts -------------------------------------------------------------------------------------------------
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int num_cus = 0;
+    int lds_per_wg = 0;     // max dynamic + static LDS bytes per workgroup
+    int lds_per_cu = 0;
+};
+
+std::mutex g_dev_mu;
+std::vector<DeviceInfo> g_dev;
+
+int device_info(int dev, DeviceInfo* out) {
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (dev >= 0 && dev < static_cast<int>(g_dev.size()) && g_dev[dev].known) {
+            *out = g_dev[dev];
+            return SDM_GX_OK;
+        }
+    }
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    DeviceInfo d;
+    d.known = true;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.lds_per_wg = static_cast<int>(prop.sharedMemPerBlock);
+    d.lds_per_cu = static_cast<int>(prop.maxSharedMemoryPerMultiProcessor);
+    if (d.lds_per_cu <= 0) d.lds_per_cu = d.lds_per_wg;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (static_cast<int>(g_dev.size()) <= dev) g_dev.resize(dev + 1);
+    g_dev[dev] = d;
+    *out = d;
+    return SDM_GX_OK;
+}
+
+int current_device(int* dev, DeviceInfo* info) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e);
+    int st = device_info(*dev, info);
+    if (st) return st;
+    return info->gfx950 ? SDM_GX_OK : SDM_GX_ERR_DEVICE;
+}
+
+// The pointer is device (or managed) memory of device `dev`.
+int on_device(const void* p, int dev) {
+    hipPointerAttribute_t a;
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();     // an unknown (host) pointer: clear the sticky error, report a device error
+        return SDM_GX_ERR_DEVICE;
+    }
+    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return SDM_GX_ERR_DEVICE;
+    if (a.device != dev) return SDM_GX_ERR_DEVICE;
+    return SDM_GX_OK;
+}
+
+// ---- planner ------------------------------------------------------------------------------------------------------
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_ri(int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16 || v == 32; }
+bool valid_rc(int v) { return v == 1 || v == 2 || v == 4; }
+bool valid_waves(int v) { return v == 1 || v == 2 || v == 4 || v == 8; }
+
+constexpr int kDefaultSlabBytes = 32 * 1024;
+
+// Fill the derived fields of a plan and check it against the shape; lds_limit: max LDS bytes per workgroup.
+int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int64_t lds_limit) {
+    if (!valid_ri(p->rows_per_wave) || !valid_rc(p->cols_per_lane) || !valid_waves(p->waves_per_wg))
+        return SDM_GX_ERR_PLAN;
+    if (p->staging != 0 && p->staging != 1) return SDM_GX_ERR_PLAN;
+    if (p->xcd_remap != 0 && p->xcd_remap != 1) return SDM_GX_ERR_PLAN;
+    if (p->rows_per_wave > C || p->slab_rows < 0) return SDM_GX_ERR_PLAN;
+    if (!sdm_gx::find_kernel(p->rows_per_wave, p->cols_per_lane, p->waves_per_wg, p->staging)) return SDM_GX_ERR_PLAN;
+    if (nchunks < 0) return SDM_GX_ERR_ARG;
+    const int64_t cw = 64 * p->cols_per_lane;
+    if (p->staging == 1) {
+        int64_t sj = p->slab_rows;
+        if (sj == 0) sj = kDefaultSlabBytes / (cw * 4);
+        if (sj > C) sj = C;
+        if (sj < 1) sj = 1;
+        p->slab_rows = static_cast<int32_t>(sj);
+        p->lds_bytes = static_cast<int32_t>(sj * cw * 4);
+        if (lds_limit > 0 && p->lds_bytes > lds_limit) return SDM_GX_ERR_LIMIT;
+    } else {
+        p->slab_rows = 0;
+        p->lds_bytes = 0;
+    }
+    const int64_t nrb = cdiv(C, p->rows_per_wave);
+    const int64_t nrg = cdiv(nrb, p->waves_per_wg);
+    const int64_t ncb = cdiv(hd, cw);
+    p->grid = nchunks * nrg * ncb;
+    return SDM_GX_OK;
+}
+
+// The planner. Columns per lane: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
+// Rows per wavefront: as many as keep the grid at >= 4 wavefronts per CU (latency hiding), between 4 and the
+// register budget (RI*RC <= 64 accumulators); never more than C. Workgroups of up to 4 wavefronts share a chunk's
+// column block.
+int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out) {
+    if (!out) return SDM_GX_ERR_ARG;
+    if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
+    if (num_cus < 1) num_cus = 256;
+    int rc = 1;
+    int64_t best_waste = cdiv(hd, 64) * 64 - hd;
+    for (int cand : {2, 4}) {
+        const int64_t w = cdiv(hd, 64 * cand) * 64 * cand - hd;
+        if (w <= best_waste) {
+            best_waste = w;
+            rc = cand;
+        }
+    }
+    const int ri_cap = rc == 1 ? 32 : (rc == 2 ? 32 : 16);
+    int ri = 1;
+    while (ri * 2 <= ri_cap && ri * 2 <= C) ri *= 2;
+    const int64_t ncb = cdiv(hd, 64 * rc);
+    const int64_t target_waves = 4LL * num_cus;
+    while (ri > 4 && nchunks * cdiv(C, ri) * ncb < target_waves) ri /= 2;
+    const int64_t nrb = cdiv(C, ri);
+    int waves = 1;
+    while (waves * 2 <= 4 && waves * 2 <= nrb) waves *= 2;
+    sdm_gx_plan_t p{};
+    p.rows_per_wave = ri;
+    p.cols_per_lane = rc;
+    p.waves_per_wg = waves;
+    p.staging = 0;
+    p.xcd_remap = 0;
+    p.slab_rows = 0;
+    int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+    if (st) return st;
+    *out = p;
+    return SDM_GX_OK;
+}
+
+// ---- launching ----------------------------------------------------------------------------------------------------
+// Chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan. Splits very large grids so that one
+// launch stays below 2^31 work-items.
+int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
+                  int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
+    if (nchunks <= 0) return SDM_GX_OK;
+    const void* fn = sdm_gx::find_kernel(p.rows_per_wave, p.cols_per_lane, p.waves_per_wg, p.staging);
+    if (!fn) return SDM_GX_ERR_PLAN;
+    const int64_t nrb = cdiv(C, p.rows_per_wave);
+    const int64_t nrg = cdiv(nrb, p.waves_per_wg);
+    const int64_t ncb = cdiv(hd, 64 * p.cols_per_lane);
+    const int64_t per_chunk = nrg * ncb;
+    const int64_t max_blocks = (int64_t(1) << 31) / (64 * p.waves_per_wg);
+    int64_t step = max_blocks / per_chunk;
+    if (step < 1) return SDM_GX_ERR_LIMIT;
+    sdm_gx::KernelArgs a;
+    a.du = du;
+    a.x = x;
+    a.dv = dv;
+    a.ld_u = ld_u;
+    a.ld_dv = ld_dv;
+    a.C = static_cast<int32_t>(C);
+    a.hd = static_cast<int32_t>(hd);
+    a.nrg = static_cast<int32_t>(nrg);
+    a.ncb = static_cast<int32_t>(ncb);
+    a.xcd_remap = p.xcd_remap;
+    a.slab_rows = p.slab_rows;
+    for (int64_t s = 0; s < nchunks; s += step) {
+        const int64_t cnt = nchunks - s < step ? nchunks - s : step;
+        a.n_begin = n_begin + s;
+        const hipError_t e = sdm_gx::launch_kernel(fn, p.waves_per_wg, static_cast<unsigned>(cnt * per_chunk),
+                                                   static_cast<unsigned>(p.lds_bytes), stream, a);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SDM_GX_OK;
+}
+
+// Plan (given or planned) for nchunks chunks on a device with `info`.
+int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, const DeviceInfo& info,
+                 sdm_gx_plan_t* out) {
+    if (given) {
+        *out = *given;
+        return complete_plan(out, nchunks, C, hd, info.lds_per_wg);
+    }
+    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out);
+}
+
+int check_device_pointers(const float* du, const float* x, const float* dv, int dev) {
+    int st = on_device(du, dev);
+    if (!st) st = on_device(x, dev);
+    if (!st) st = on_device(dv, dev);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_gx_check(const float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv, int64_t N,
+                 int64_t ti, int64_t P, int64_t C, int64_t hd) {
+    return check_args(d_u, ld_u, x, d_dv, ld_dv, N, ti, P, C, hd);
+}
+
+int sdm_gx_gemm_ex(float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv, int64_t N, int64_t ti,
+                   int64_t P, int64_t C, int64_t hd, const sdm_gx_plan_t* plan, void* stream) {
+    int st = check_args(d_u, ld_u, x, d_dv, ld_dv, N, ti, P, C, hd);
+    if (st) return st;
+    int dev = 0;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info))) return st;
+    if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
+    sdm_gx_plan_t p;
+    if ((st = resolve_plan(plan, P, C, hd, info, &p))) return st;
+    return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, static_cast<hipStream_t>(stream));
+}
+
+int sdm_gx_gemm(float* d_u, const float* x, const float* d_dv, int64_t ti, int64_t P, int64_t C, int64_t hd,
+                void* stream) {
+    if (P < 1) return SDM_GX_ERR_SHAPE;
+    if (ti < 0 || ti >= (SDM_GX_N_LIMIT - 1) / P) return SDM_GX_ERR_STEP;    // (ti + 1) * P < 2^31
+    const int64_t N = (ti + 1) * P;
+    return sdm_gx_gemm_ex(d_u, hd, x, d_dv, hd, N, ti, P, C, hd, nullptr, stream);
+}
+
+int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv, int64_t N,
+                      int64_t P, int64_t C, int64_t hd, int64_t ti_begin, int64_t ti_end, int32_t mode,
+                      const sdm_gx_plan_t* plan, void* stream) {
+    if (mode != SDM_GX_STEPS_FORWARD && mode != SDM_GX_STEPS_REVERSE && mode != SDM_GX_STEPS_FUSED)
+        return SDM_GX_ERR_ARG;
+    if (ti_begin < 0 || ti_end < ti_begin) return SDM_GX_ERR_STEP;
+    // validate once, at the last step of the range (its bound covers every earlier step)
+    int st = check_args(d_u, ld_u, x, d_dv, ld_dv, N, ti_end > ti_begin ? ti_end - 1 : ti_begin, P, C, hd);
+    if (st) return st;
+    if (ti_end == ti_begin) return SDM_GX_OK;
+    int dev = 0;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info))) return st;
+    if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    sdm_gx_plan_t p;
+    if (mode == SDM_GX_STEPS_FUSED) {
+        const int64_t nchunks = (ti_end - ti_begin) * P;
+        if ((st = resolve_plan(plan, nchunks, C, hd, info, &p))) return st;
+        return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti_begin * P, nchunks, C, hd, s);
+    }
+    if ((st = resolve_plan(plan, P, C, hd, info, &p))) return st;
+    for (int64_t k = 0; k < ti_end - ti_begin; ++k) {
+        const int64_t ti = mode == SDM_GX_STEPS_FORWARD ? ti_begin + k : ti_end - 1 - k;
+        if ((st = launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, s))) return st;
+    }
+    return SDM_GX_OK;
+}
+
+int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_plan_t* out) {
+    if (!out) return SDM_GX_ERR_ARG;
+    int dev = device;
+    if (dev < 0) {
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    DeviceInfo info;
+    int st = device_info(dev, &info);
+    if (st) return st;
+    if (!info.gfx950) return SDM_GX_ERR_DEVICE;
+    if ((st = plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out))) return st;
+    const void* fn = sdm_gx::find_kernel(out->rows_per_wave, out->cols_per_lane, out->waves_per_wg, out->staging);
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * out->waves_per_wg, out->lds_bytes) ==
+        hipSuccess)
+        out->wgs_per_cu = blocks;
+    else
+        (void)hipGetLastError();
+    return SDM_GX_OK;
+}
+
+int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int32_t num_cus, int32_t lds_per_cu,
+                    sdm_gx_plan_t* out) {
+    return plan_for(nchunks, C, hd, num_cus, lds_per_cu, out);
+}
+
+int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd, int32_t lds_per_cu) {
+    if (!plan) return SDM_GX_ERR_ARG;
+    if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT) return SDM_GX_ERR_SHAPE;
+    return complete_plan(plan, nchunks, C, hd, lds_per_cu);
+}
+
+int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
+                   int64_t N, int64_t P, int64_t C, int64_t hd, int64_t ti_max, const sdm_gx_plan_t* plan) {
+    if (!out) return SDM_GX_ERR_ARG;
+    std::memset(out, 0, sizeof(*out));
+    int st = check_args(d_u, ld_u, x, d_dv, ld_dv, N, ti_max, P, C, hd);
+    if (st) return st;
+    int dev = 0;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info))) return st;
+    if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
+    sdm_gx_launch_t l;
+    std::memset(&l, 0, sizeof(l));
+    if ((st = resolve_plan(plan, P, C, hd, info, &l.plan_step))) return st;
+    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, info, &l.plan_fused))) return st;
+    l.device = dev;
+    l.d_u = d_u;
+    l.x = x;
+    l.d_dv = d_dv;
+    l.ld_u = ld_u;
+    l.ld_dv = ld_dv;
+    l.N = N;
+    l.P = P;
+    l.C = C;
+    l.hd = hd;
+    l.ti_max = ti_max;
+    l.magic = kLaunchMagic;
+    *out = l;
+    return SDM_GX_OK;
+}
+
+static int prepared_ok(const sdm_gx_launch_t* l) {
+    if (!l || l->magic != kLaunchMagic) return SDM_GX_ERR_PLAN;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev != l->device) return SDM_GX_ERR_DEVICE;
+    return SDM_GX_OK;
+}
+
+int sdm_gx_launch(const sdm_gx_launch_t* prepared, int64_t ti, void* stream) {
+    int st = prepared_ok(prepared);
+    if (st) return st;
+    const sdm_gx_launch_t& l = *prepared;
+    if (ti < 0 || ti > l.ti_max) return SDM_GX_ERR_STEP;
+    return launch_chunks(l.plan_step, l.d_u, l.ld_u, l.x, l.d_dv, l.ld_dv, ti * l.P, l.P, l.C, l.hd,
+                         static_cast<hipStream_t>(stream));
+}
+
+int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64_t ti_end, void* stream) {
+    int st = prepared_ok(prepared);
+    if (st) return st;
+    const sdm_gx_launch_t& l = *prepared;
+    if (ti_begin < 0 || ti_end < ti_begin || ti_end > l.ti_max + 1) return SDM_GX_ERR_STEP;
+    return launch_chunks(l.plan_fused, l.d_u, l.ld_u, l.x, l.d_dv, l.ld_dv, ti_begin * l.P, (ti_end - ti_begin) * l.P,
+                         l.C, l.hd, static_cast<hipStream_t>(stream));
+}
+
+int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]) {
+    if (!plan || !out) return SDM_GX_ERR_ARG;
+    const void* fn = sdm_gx::find_kernel(plan->rows_per_wave, plan->cols_per_lane, plan->waves_per_wg, plan->staging);
+    if (!fn) return SDM_GX_ERR_PLAN;
+    hipFuncAttributes a;
+    hipError_t e = hipFuncGetAttributes(&a, fn);
+    if (e != hipSuccess) return hip_fail(e);
+    out[0] = a.numRegs;
+    out[1] = static_cast<int64_t>(a.localSizeBytes);
+    out[2] = static_cast<int64_t>(a.sharedSizeBytes);
+    out[3] = a.maxThreadsPerBlock;
+    out[4] = plan->lds_bytes;
+    return SDM_GX_OK;
+}
+
+const char* sdm_gx_strerror(int code) {
+    switch (code) {
+        case SDM_GX_OK: return "ok";
+        case SDM_GX_ERR_NULL: return "a required pointer is NULL";
+        case SDM_GX_ERR_SHAPE: return "shape out of range (need 1 <= C <= 256, 1 <= hd < 2^20, 1 <= P, 1 <= N < 2^31)";
+        case SDM_GX_ERR_STEP: return "step out of range (need 1 <= P <= N and 0 <= ti < N / P)";
+        case SDM_GX_ERR_ALIGN: return "pointer not 4-byte aligned";
+        case SDM_GX_ERR_OVERLAP: return "d_u overlaps x or d_dv (the in-place update needs disjoint operands)";
+        case SDM_GX_ERR_STRIDE: return "row stride out of range (need hd <= ld < 2^31)";
+        case SDM_GX_ERR_LIMIT: return "launch exceeds a device limit";
+        case SDM_GX_ERR_HIP: return "HIP runtime error (see sdm_gx_last_hip_error)";
+        case SDM_GX_ERR_PLAN: return "invalid plan or prepared launch";
+        case SDM_GX_ERR_DEVICE: return "no gfx950 device, or a pointer / prepared launch is not on the current device";
+        case SDM_GX_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int sdm_gx_last_hip_error(void) { return g_last_hip_error; }
+
+int sdm_gx_abi_version(void) { return SDM_GX_ABI_VERSION; }
+
+}  // extern "C"

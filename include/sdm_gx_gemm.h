@@ -1,0 +1,183 @@
+/*
+ * sdm_gx_gemm -- deterministic FP32 per-step d_u update for MI355X (gfx950), C ABI.
+ *
+ * The operation (page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py", module docstring;
+ * gx_gemm_kernel's j-chain and epilogue on the same page):
+ *
+ *   for every chunk n = ti*P + p (0 <= p < P) of step ti, row i < C and column c < hd:
+ *       acc = +0
+ *       for j = 0, 1, ..., C-1 in this order:   acc = fmaf(x[n, j, i], d_dv[n, j, c], acc)
+ *       d_u[n, i, c] = d_u[n, i, c] + acc        (one separately rounded IEEE binary32 add, in place)
+ *
+ * Every fused multiply-add and the final add round to nearest even and keep subnormals. Each output element is
+ * computed by one GPU lane running exactly that chain, so results are bit-identical for every launch plan, step
+ * order and run, and equal to the CPU definition wherever the result is not NaN (NaN results are NaN on both
+ * sides; their payload is not specified).
+ *
+ * Memory layout (FP32, row-major; element offsets):
+ *   x     [N][C][C]               x[n, j, i]    at (n*C + j)*C + i        (contiguous; used transposed)
+ *   d_dv  [N][C] rows of ld_dv    d_dv[n, j, c] at (n*C + j)*ld_dv + c    (c < hd <= ld_dv)
+ *   d_u   [N][C] rows of ld_u     d_u[n, i, c]  at (n*C + i)*ld_u + c     (c < hd <= ld_u), updated in place
+ * Only columns c < hd of the chunks of the requested steps are read (d_dv, d_u) or written (d_u); x is read for
+ * those chunks only. The library never touches memory past element (N*C - 1)*ld + hd - 1 of d_u / d_dv, nor the
+ * padding columns hd..ld-1 of any row. Chunks n >= (N / P) * P belong to no step and are never touched.
+ *
+ * Ownership and execution: every pointer is caller-owned device memory of the current HIP device (for example a
+ * torch tensor's data_ptr()). The library allocates nothing on the caller's behalf, keeps no pointer after a call
+ * returns (except inside a caller-owned sdm_gx_launch_t), and runs its kernels asynchronously on the caller's
+ * stream (`stream` is a hipStream_t; NULL means the null stream). Calls on the same stream run in order. d_u must
+ * not overlap x or d_dv.
+ *
+ * Errors: every entry point returns an int status (sdm_gx_status); no exception crosses the ABI. Argument checks
+ * run on the host before anything is launched; on an error nothing is launched and no memory is touched.
+ * SDM_GX_ERR_HIP carries the HIP runtime error of the failing call in sdm_gx_last_hip_error() (per host thread).
+ * All entry points are thread-safe.
+ */
+#ifndef SDM_GX_GEMM_H
+#define SDM_GX_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDM_GX_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SDM_GX_API __attribute__((visibility("default")))
+#else
+#define SDM_GX_API
+#endif
+
+/* Shape limits (the page's host entry gx_gemm and its supported(): 1 <= C <= 256, 1 <= hd < 2^20,
+ * 1 <= P <= N < 2^31). */
+#define SDM_GX_MAX_C 256
+#define SDM_GX_HD_LIMIT (1 << 20)          /* hd < SDM_GX_HD_LIMIT */
+#define SDM_GX_N_LIMIT (INT64_C(1) << 31)  /* N < SDM_GX_N_LIMIT */
+#define SDM_GX_LD_LIMIT (INT64_C(1) << 31) /* ld_u, ld_dv < SDM_GX_LD_LIMIT */
+
+typedef enum sdm_gx_status {
+    SDM_GX_OK = 0,             /* done (also: nothing to do) */
+    SDM_GX_ERR_NULL = -1,      /* a required pointer is NULL */
+    SDM_GX_ERR_SHAPE = -2,     /* C not in [1, 256], hd not in [1, 2^20), P < 1, N not in [1, 2^31) */
+    SDM_GX_ERR_STEP = -3,      /* ti < 0, ti >= N / P, P > N, or an empty / out-of-range step range */
+    SDM_GX_ERR_ALIGN = -4,     /* a pointer is not 4-byte aligned */
+    SDM_GX_ERR_OVERLAP = -5,   /* d_u overlaps x or d_dv */
+    SDM_GX_ERR_STRIDE = -6,    /* ld_u or ld_dv < hd, or >= 2^31 */
+    SDM_GX_ERR_LIMIT = -7,     /* the launch exceeds a device limit (LDS per workgroup) */
+    SDM_GX_ERR_HIP = -8,       /* a HIP runtime call failed: see sdm_gx_last_hip_error() */
+    SDM_GX_ERR_PLAN = -9,      /* a plan / prepared launch is malformed or does not fit this shape */
+    SDM_GX_ERR_DEVICE = -10,   /* no usable gfx950 device, pointers not on the current device, or a prepared
+                                  launch used on another device */
+    SDM_GX_ERR_ARG = -11       /* any other invalid argument (unknown mode, NULL output struct, ...) */
+} sdm_gx_status;
+
+/* A launch plan: how output tiles map onto wavefronts and workgroups. Results never depend on it.
+ *   rows_per_wave  RI: output rows one wavefront owns (1, 2, 4, 8, 16 or 32; RI <= C)
+ *   cols_per_lane  RC: adjacent output columns one lane owns (1, 2 or 4); a wavefront covers 64*RC columns
+ *   waves_per_wg   wavefronts per workgroup (1, 2, 4 or 8); they take consecutive row blocks of one chunk and
+ *                  column block
+ *   staging        0: each wavefront reads its d_dv columns straight from global memory;
+ *                  1: the workgroup stages its d_dv column block in LDS once and every wavefront reads it there
+ *   xcd_remap      1: workgroup ids are permuted so that the workgroups of one chunk run on one XCD (one L2)
+ *   slab_rows      staging 1: d_dv rows per LDS slab (0: the planner's choice; clamped to C)
+ *   lds_bytes      (output of the planner) dynamic LDS bytes per workgroup
+ *   wgs_per_cu     (output of the planner) workgroups per CU that can be resident (0 if not known)
+ *   grid           (output of the planner) workgroups for the chunk count it was planned for */
+typedef struct sdm_gx_plan {
+    int32_t rows_per_wave;
+    int32_t cols_per_lane;
+    int32_t waves_per_wg;
+    int32_t staging;
+    int32_t xcd_remap;
+    int32_t slab_rows;
+    int32_t lds_bytes;
+    int32_t wgs_per_cu;
+    int64_t grid;
+} sdm_gx_plan_t;
+
+/* One step ti of the update with contiguous rows (ld_u = ld_dv = hd), planned automatically. There is no N: the
+ * caller vouches that chunks 0 .. (ti+1)*P - 1 exist in all three arrays, and the checks of sdm_gx_gemm_ex run with
+ * N = (ti+1)*P (so P >= 1, ti >= 0, (ti+1)*P < 2^31, and no overlap among those chunks).
+ * Same operation as the page's host entry gx_gemm (its plain, non-PDL launch). */
+SDM_GX_API int sdm_gx_gemm(float* d_u, const float* x, const float* d_dv, int64_t ti, int64_t P, int64_t C,
+                           int64_t hd, void* stream);
+
+/* One step ti with row strides and the full chunk count N (checks 0 <= ti < N / P and whole-array overlap, as the
+ * page's gx_gemm does). plan == NULL: the planner chooses; otherwise the given plan is validated and used. */
+SDM_GX_API int sdm_gx_gemm_ex(float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
+                              int64_t N, int64_t ti, int64_t P, int64_t C, int64_t hd, const sdm_gx_plan_t* plan,
+                              void* stream);
+
+/* Multi-step driver (the page's per-backward plan gx_gemm_plan / gx_gemm_plan_launch and make_step's step loop):
+ * validates once for steps ti_begin .. ti_end - 1, then
+ *   SDM_GX_STEPS_FORWARD  one launch per step, ti ascending
+ *   SDM_GX_STEPS_REVERSE  one launch per step, ti descending (the backward's order)
+ *   SDM_GX_STEPS_FUSED    one launch covering every chunk of those steps
+ * All three give identical bits: steps update disjoint chunks and each element is still one fixed chain.
+ * ti_begin == ti_end is a no-op. */
+#define SDM_GX_STEPS_FORWARD 0
+#define SDM_GX_STEPS_REVERSE 1
+#define SDM_GX_STEPS_FUSED 2
+SDM_GX_API int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
+                                 int64_t N, int64_t P, int64_t C, int64_t hd, int64_t ti_begin, int64_t ti_end,
+                                 int32_t mode, const sdm_gx_plan_t* plan, void* stream);
+
+/* Argument checks of sdm_gx_gemm_ex without touching any device (no HIP call): the status the launch would return
+ * before reaching the GPU, except for device-membership checks. Mirrors the page's gx_gemm checks. */
+SDM_GX_API int sdm_gx_check(const float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
+                            int64_t N, int64_t ti, int64_t P, int64_t C, int64_t hd);
+
+/* The planner for `nchunks` chunks of shape (C, hd) on HIP device `device` (-1: current device). Fills *out. */
+SDM_GX_API int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_plan_t* out);
+
+/* The same planner with the device facts given explicitly (no HIP call): compute units and LDS bytes per CU. */
+SDM_GX_API int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int32_t num_cus, int32_t lds_per_cu,
+                               sdm_gx_plan_t* out);
+
+/* Validate a caller-made plan for shape (C, hd) and fill its output fields for `nchunks` chunks. */
+SDM_GX_API int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd,
+                                    int32_t lds_per_cu);
+
+/* A prepared step launch (the page's GemmPlan): everything is validated once for every ti <= ti_max, then
+ * sdm_gx_launch issues step ti with only ti changed. The struct is caller-owned plain data; it holds the three
+ * device pointers, so it is valid while those buffers are. */
+typedef struct sdm_gx_launch {
+    uint64_t magic;
+    int32_t device;
+    int32_t reserved0;
+    float* d_u;
+    const float* x;
+    const float* d_dv;
+    int64_t ld_u, ld_dv, N, P, C, hd, ti_max;
+    sdm_gx_plan_t plan_step;   /* used by sdm_gx_launch (P chunks) */
+    sdm_gx_plan_t plan_fused;  /* used by sdm_gx_launch_fused (planned for (ti_max+1)*P chunks) */
+} sdm_gx_launch_t;
+
+/* plan == NULL: the planner chooses both plans; otherwise the given plan is validated and used for both. */
+SDM_GX_API int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* x, const float* d_dv,
+                              int64_t ld_dv, int64_t N, int64_t P, int64_t C, int64_t hd, int64_t ti_max,
+                              const sdm_gx_plan_t* plan);
+/* Issue step ti (0 <= ti <= ti_max) of a prepared launch on `stream`; the current device must be the prepared one. */
+SDM_GX_API int sdm_gx_launch(const sdm_gx_launch_t* prepared, int64_t ti, void* stream);
+/* Issue steps ti_begin .. ti_end - 1 of a prepared launch as ONE launch (every ti <= ti_max). */
+SDM_GX_API int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64_t ti_end, void* stream);
+
+/* Resource usage of the kernel instance a plan selects (the page's gx_gemm_attrs): out[0] architectural VGPRs per
+ * lane, out[1] private (scratch) bytes per lane, out[2] static LDS bytes, out[3] max threads per workgroup,
+ * out[4] the plan's dynamic LDS bytes. Needs a device. */
+SDM_GX_API int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]);
+
+/* Text for a status code (static storage). */
+SDM_GX_API const char* sdm_gx_strerror(int code);
+/* The HIP error (hipError_t value) behind the last SDM_GX_ERR_HIP on this host thread; 0 if none. */
+SDM_GX_API int sdm_gx_last_hip_error(void);
+/* SDM_GX_ABI_VERSION of the loaded library. */
+SDM_GX_API int sdm_gx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_GX_GEMM_H */

@@ -1,0 +1,179 @@
+"""C ABI tests that need no GPU: the library loads and exports every function the header declares, the ctypes
+structs match the C layout, argument checks return the documented status codes, and the planner only emits plans
+the kernels support."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import deterministic_fp32_gemm_amd as g
+from deterministic_fp32_gemm_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm_gx_gemm.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SDM_GX_API\s+(?:const\s+)?\w+\*?\s+\*?(sdm_gx_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    assert "sdm_gx_gemm" in names and "sdm_gx_gemm_steps" in names and len(names) >= 14
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == header_functions()
+
+
+def test_only_the_c_abi_is_exported():
+    """Exported functions are exactly the C ABI (kernel handle variables, type V, are the HIP runtime's)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True, check=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if ln.split() and ln.split()[1] in ("T", "W")}
+    assert exported == set(header_functions()), exported ^ set(header_functions())
+
+
+def test_abi_version():
+    assert g.sdm_gx_abi_version() == 1
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "sdm_gx_gemm.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
+         sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
+         offsetof(sdm_gx_launch_t, plan_fused));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals == [ctypes.sizeof(g.sdm_gx_plan_t), g.sdm_gx_plan_t.grid.offset, ctypes.sizeof(g.sdm_gx_launch_t),
+                    g.sdm_gx_launch_t.ti_max.offset, g.sdm_gx_launch_t.plan_step.offset,
+                    g.sdm_gx_launch_t.plan_fused.offset]
+
+
+def test_strerror_covers_every_code():
+    for code in range(0, -12, -1):
+        assert g.sdm_gx_strerror(code) != "unknown status"
+    assert g.sdm_gx_strerror(-99) == "unknown status"
+
+
+# ---- argument checks (addresses are plain integers: nothing is dereferenced) -------------------------------------
+U, X, V = 1 << 32, 1 << 36, 1 << 40        # far-apart fake device addresses
+
+
+def chk(**kw):
+    a = dict(d_u=U, ld_u=64, x=X, d_dv=V, ld_dv=64, N=8, ti=0, P=4, C=64, hd=64)
+    a.update(kw)
+    return g.sdm_gx_check(a["d_u"], a["ld_u"], a["x"], a["d_dv"], a["ld_dv"], a["N"], a["ti"], a["P"], a["C"],
+                          a["hd"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, g.SDM_GX_OK),
+    (dict(ti=1), g.SDM_GX_OK),
+    (dict(d_u=0), g.SDM_GX_ERR_NULL),
+    (dict(x=0), g.SDM_GX_ERR_NULL),
+    (dict(d_dv=0), g.SDM_GX_ERR_NULL),
+    (dict(C=0), g.SDM_GX_ERR_SHAPE),
+    (dict(C=257), g.SDM_GX_ERR_SHAPE),
+    (dict(C=256, ld_u=64, hd=64), g.SDM_GX_OK),
+    (dict(hd=0), g.SDM_GX_ERR_SHAPE),
+    (dict(hd=1 << 20, ld_u=1 << 20, ld_dv=1 << 20), g.SDM_GX_ERR_SHAPE),
+    (dict(hd=(1 << 20) - 1, ld_u=1 << 20, ld_dv=1 << 20, N=1, P=1), g.SDM_GX_OK),
+    (dict(N=0), g.SDM_GX_ERR_SHAPE),
+    (dict(N=1 << 31), g.SDM_GX_ERR_SHAPE),
+    (dict(P=0), g.SDM_GX_ERR_SHAPE),
+    (dict(ld_u=63), g.SDM_GX_ERR_STRIDE),
+    (dict(ld_dv=63), g.SDM_GX_ERR_STRIDE),
+    (dict(ld_u=1 << 31), g.SDM_GX_ERR_STRIDE),
+    (dict(P=9), g.SDM_GX_ERR_STEP),
+    (dict(ti=-1), g.SDM_GX_ERR_STEP),
+    (dict(ti=2), g.SDM_GX_ERR_STEP),
+    (dict(ti=(1 << 62)), g.SDM_GX_ERR_STEP),
+    (dict(N=9, P=4, ti=2), g.SDM_GX_ERR_STEP),      # the trailing chunk 8 belongs to no step
+    (dict(d_u=U + 2), g.SDM_GX_ERR_ALIGN),
+    (dict(x=X + 1), g.SDM_GX_ERR_ALIGN),
+    (dict(d_dv=V + 6), g.SDM_GX_ERR_ALIGN),
+    (dict(d_u=U + 4), g.SDM_GX_OK),                  # 4-byte alignment is enough
+    (dict(x=U + 4 * 100), g.SDM_GX_ERR_OVERLAP),
+    (dict(d_dv=U + 4 * (8 * 64 * 64 - 1)), g.SDM_GX_ERR_OVERLAP),
+    (dict(d_dv=U + 4 * 8 * 64 * 64), g.SDM_GX_OK),   # adjacent, not overlapping
+    (dict(x=U - 4 * 8 * 64 * 64), g.SDM_GX_OK),      # x ends exactly where d_u starts
+    (dict(x=U - 4 * 8 * 64 * 64 + 4), g.SDM_GX_ERR_OVERLAP),
+    (dict(ld_u=100, d_dv=U + 4 * ((8 * 64 - 1) * 100 + 64)), g.SDM_GX_OK),   # extent ends at the last row's hd
+])
+def test_check_codes(kw, code):
+    assert chk(**kw) == code
+
+
+def test_plan_for_emits_supported_plans():
+    shapes = [(C, hd) for C in (1, 2, 3, 4, 5, 16, 17, 31, 64, 100, 128, 200, 256)
+              for hd in (1, 3, 4, 63, 64, 65, 100, 128, 129, 200, 256, 257, 1000, 4100)]
+    for nchunks in (0, 1, 7, 128, 4096):
+        for C, hd in shapes:
+            p = g.sdm_gx_plan_for(nchunks, C, hd)
+            assert p.rows_per_wave in (1, 2, 4, 8, 16, 32) and p.rows_per_wave <= C
+            assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
+            assert p.waves_per_wg in (1, 2, 4, 8)
+            nrb = -(-C // p.rows_per_wave)
+            nrg = -(-nrb // p.waves_per_wg)
+            ncb = -(-hd // (64 * p.cols_per_lane))
+            assert p.grid == nchunks * nrg * ncb
+            assert p.lds_bytes <= 64 * 1024
+
+
+@pytest.mark.parametrize("bad", [
+    dict(rows_per_wave=3), dict(rows_per_wave=64), dict(cols_per_lane=3), dict(waves_per_wg=3),
+    dict(waves_per_wg=16), dict(staging=2), dict(xcd_remap=2), dict(slab_rows=-1),
+    dict(rows_per_wave=32, cols_per_lane=4),
+])
+def test_plan_complete_rejects(bad):
+    p = g.make_plan(8, 1, 4)
+    for k, v in bad.items():
+        setattr(p, k, v)
+    with pytest.raises(ValueError):
+        g.sdm_gx_plan_complete(p, 4, 64, 64)
+
+
+def test_plan_complete_rows_beyond_c():
+    with pytest.raises(ValueError):
+        g.sdm_gx_plan_complete(g.make_plan(16, 1, 1), 4, 8, 64)
+    assert g.sdm_gx_plan_complete(g.make_plan(8, 1, 1), 4, 8, 64).grid == 4
+
+
+def test_plan_complete_lds_limit():
+    p = g.sdm_gx_plan_complete(g.make_plan(8, 2, 4, staging=1, slab_rows=256), 4, 256, 256, 160 * 1024)
+    assert p.slab_rows == 256 and p.lds_bytes == 256 * 128 * 4
+    with pytest.raises(RuntimeError):
+        g.sdm_gx_plan_complete(g.make_plan(8, 2, 4, staging=1, slab_rows=256), 4, 256, 256, 64 * 1024)
+    p = g.sdm_gx_plan_complete(g.make_plan(8, 4, 4, staging=1, slab_rows=300), 4, 100, 256, 160 * 1024)
+    assert p.slab_rows == 100                       # clamped to C
+    p = g.sdm_gx_plan_complete(g.make_plan(8, 4, 4, staging=1), 4, 256, 256)
+    assert p.slab_rows == 32 and p.lds_bytes == 32 * 1024
+
+
+def test_tensor_layout_rejects_bad_shapes():
+    torch = pytest.importorskip("torch")
+    from deterministic_fp32_gemm_amd import tensor_layout
+    x = torch.zeros(4, 8, 8)
+    du = torch.zeros(4, 8, 12)[:, :, :10]
+    dv = torch.zeros(32, 10)
+    assert tensor_layout(du, x, dv) == (4, 8, 10, 12, 10)
+    with pytest.raises(ValueError):
+        tensor_layout(du, x.transpose(1, 2), dv)
+    with pytest.raises(ValueError):
+        tensor_layout(du, x, torch.zeros(31, 10))

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle, element by element.
+
+Bar: every non-NaN output bit-identical to the oracle, NaN outputs NaN on both sides, padding columns and chunks
+outside the requested steps untouched (bit for bit).
+"""
+
+import numpy as np
+import pytest
+
+import deterministic_fp32_gemm_amd as g
+from deterministic_fp32_gemm_amd import inputs
+from tests.gpu_util import DeviceCase, assert_matches, expected, say, workload_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the parity tests need an MI355X")
+    arch = torch.cuda.get_device_properties(0).gcnArchName
+    assert arch.startswith("gfx950"), arch
+    g.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_steps(case: DeviceCase, P, ti_begin, ti_end, mode, plan=None):
+    du, ld_u, x, dv, ld_dv, N = case.args()
+    g.sdm_gx_gemm_steps(du, ld_u, x, dv, ld_dv, N, P, case.C, case.hd, ti_begin, ti_end, mode, plan)
+    return case.result()
+
+
+# ---- the five workloads ----------------------------------------------------------------------------------------------
+WORKLOAD_PATTERNS = [(1, p) for p in inputs.ALL_PATTERNS] + [(2, p) for p in inputs.ALL_PATTERNS] + \
+    [(3, p) for p in inputs.ALL_PATTERNS] + [(4, "normal"), (4, "probe_special"), (4, "probe_denormal")] + \
+    [(5, "normal"), (5, "probe_special"), (5, "nan")]
+
+
+@pytest.mark.parametrize("key,pattern", WORKLOAD_PATTERNS, ids=lambda v: str(v))
+def test_workload_steps_in_order(key, pattern):
+    """All T steps in order ti = 0..T-1 (one launch per step), then the whole d_u against the oracle."""
+    w, case = workload_case(key, pattern)
+    say(f"workload {key} pattern {pattern}: N={w.N} P={w.P} C={w.C} hd={w.hd} ld={w.ld}")
+    got = run_steps(case, w.P, 0, w.T, g.SDM_GX_STEPS_FORWARD)
+    want = expected(case.x_h, case.dv_h, case.du_h, w.hd, 0, w.N)
+    assert_matches(got, want, case.du_h, w.hd, f"workload {key} {pattern}")
+
+
+@pytest.mark.parametrize("pattern", inputs.PATTERNS)
+def test_workload3_after_every_step(pattern):
+    """The six value patterns, compared with the oracle after every one of the T steps."""
+    w, case = workload_case(3, pattern)
+    want = case.du_h.copy()
+    import oracle
+    for ti in range(w.T):
+        say(f"workload 3 pattern {pattern} step {ti}")
+        g.sdm_gx_gemm_ex(*case.args()[:5], w.N, ti, w.P, w.C, w.hd)
+        oracle.gx_gemm_chunks(want, case.x_h, case.dv_h, ti * w.P, (ti + 1) * w.P, w.hd, threads=8)
+        assert_matches(case.result(), want, case.du_h, w.hd, f"workload 3 {pattern} after step {ti}")
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_workload_bench_launch(key):
+    """The launch configuration the benchmark times (a prepared launch, all T steps fused into one launch, repeated
+    three times back to back so d_u accumulates) against the oracle applying the same three sweeps."""
+    import torch
+    w, case = workload_case(key)
+    say(f"workload {key} fused x3")
+    N, C, hd = w.N, w.C, w.hd
+    du_t = case.du.view(N, C, w.ld)[:, :, :hd]
+    dv_t = case.dv.view(N, C, w.ld)[:, :, :hd]
+    x_t = case.x.view(N, C, C)
+    step = g.make_step(du_t, x_t, dv_t, w.P)
+    for _ in range(3):
+        step.fused(0, w.T)
+    torch.cuda.synchronize()
+    want = case.du_h.copy()
+    for _ in range(3):
+        want = expected(case.x_h, case.dv_h, want, hd, 0, N)
+    assert_matches(case.result(), want, case.du_h, hd, f"workload {key} fused x3")
+
+
+# ---- every plan gives the same bits --------------------------------------------------------------------------------
+def all_plans(C):
+    for ri in (1, 2, 4, 8, 16, 32):
+        if ri > C:
+            continue
+        for rc in (1, 2, 4):
+            if ri * rc > 64:
+                continue
+            for waves in (1, 2, 4, 8):
+                for staging in (0, 1):
+                    for xcd in (0, 1):
+                        slab = (0, 5) if staging else (0,)
+                        for sj in slab:
+                            yield g.make_plan(ri, rc, waves, staging, xcd, sj)
+
+
+@pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8)])
+def test_every_plan_is_bit_identical(C, hd, ld, res):
+    N, P = 6, 3
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C + hd)
+    case = DeviceCase(x, dv, du, hd, res_u=res, res_v=res, res_x=(res * 3) % 256)
+    want = expected(x, dv, du, hd, 0, N)
+    n = 0
+    for plan in all_plans(C):
+        case.reset()
+        say(f"plan {plan} C={C} hd={hd} ld={ld}")
+        got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FORWARD, plan)
+        assert_matches(got, want, du, hd, f"plan {plan}")
+        n += 1
+    assert n > 50
+
+
+# ---- driver modes ----------------------------------------------------------------------------------------------------
+def test_driver_modes_agree():
+    N, P, C, hd, ld = 14, 4, 24, 70, 72              # N % P != 0: chunks 12, 13 belong to no step
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_large", seed=5)
+    case = DeviceCase(x, dv, du, hd, res_u=12, res_v=20, res_x=4)
+    want = expected(x, dv, du, hd, 0, (N // P) * P)
+    for mode in (g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_REVERSE, g.SDM_GX_STEPS_FUSED):
+        case.reset()
+        say(f"mode {mode}")
+        assert_matches(run_steps(case, P, 0, N // P, mode), want, du, hd, f"mode {mode}")
+    # prepared launches: per step in reverse (the backward's order), and fused
+    import torch
+    du_t = case.du.view(N, C, ld)[:, :, :hd]
+    dv_t = case.dv.view(N, C, ld)[:, :, :hd]
+    step = g.make_step(du_t, case.x.view(N, C, C), dv_t, P)
+    case.reset()
+    for ti in reversed(range(N // P)):
+        step(ti)
+    assert_matches(case.result(), want, du, hd, "prepared per step")
+    case.reset()
+    step.fused(0, 1)
+    step.fused(1, N // P)
+    assert_matches(case.result(), want, du, hd, "prepared fused")
+    torch.cuda.synchronize()
+
+
+def test_contiguous_entry_point():
+    """sdm_gx_gemm (no N, rows of hd floats) on step ti: only that step's chunks change."""
+    N, P, C, hd, ti = 9, 3, 32, 96, 2
+    x, dv, du = inputs.shape_inputs(N, C, hd, None, "normal", seed=6)
+    case = DeviceCase(x, dv, du, hd)
+    g.sdm_gx_gemm(case.du, case.x, case.dv, ti, P, C, hd)
+    want = expected(x, dv, du, hd, ti * P, (ti + 1) * P)
+    assert_matches(case.result(), want, du, hd, "sdm_gx_gemm")
+
+
+# ---- edge shapes and alignment -------------------------------------------------------------------------------------
+EDGE = [  # N, P, C, hd, ld, res_u, res_x, res_v, pattern
+    (1, 1, 1, 1, 1, 0, 0, 0, "normal"),
+    (2, 1, 1, 5, 7, 4, 8, 12, "probe_special"),
+    (3, 3, 3, 5, 5, 4, 4, 4, "normal"),
+    (2, 2, 256, 1, 1, 0, 0, 0, "normal"),            # longest chain, one column
+    (2, 2, 256, 260, 263, 4, 0, 8, "probe_cancel"),  # longest chain, ragged columns
+    (4, 2, 17, 4100, 4100, 0, 0, 0, "normal"),       # many column blocks with a tail
+    (5, 2, 63, 129, 131, 252, 248, 244, "probe_zeros"),
+    (7, 7, 100, 3, 3, 8, 4, 0, "probe_denormal"),
+    (3, 1, 33, 255, 255, 4, 4, 4, "inf"),
+]
+
+
+@pytest.mark.parametrize("N,P,C,hd,ld,ru,rx,rv,pattern", EDGE)
+def test_edge_shapes(N, P, C, hd, ld, ru, rx, rv, pattern):
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, pattern, seed=N + C + hd)
+    case = DeviceCase(x, dv, du, hd, res_u=ru, res_x=rx, res_v=rv)
+    say(f"edge N={N} P={P} C={C} hd={hd} ld={ld} res=({ru},{rx},{rv}) {pattern}")
+    got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED)
+    want = expected(x, dv, du, hd, 0, (N // P) * P)
+    assert_matches(got, want, du, hd, "edge")
+
+
+@pytest.mark.parametrize("res", [(0, 0, 0), (4, 0, 0), (0, 4, 0), (0, 0, 4), (4, 8, 12), (12, 4, 8), (60, 124, 252),
+                                 (128, 64, 32)])
+def test_alignment_classes(res):
+    """Every 4-byte residue class of the three base pointers (mod 256) gives the same bits; a 16-byte-aligned row
+    stride keeps the class, an odd stride walks through all of them across rows."""
+    N, P, C, hd = 4, 2, 32, 128
+    for ld in (128, 129):
+        x, dv, du = inputs.shape_inputs(N, C, hd, ld, "normal", seed=ld)
+        case = DeviceCase(x, dv, du, hd, res_u=res[0], res_x=res[1], res_v=res[2])
+        say(f"alignment {res} ld={ld}")
+        got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FORWARD)
+        assert_matches(got, expected(x, dv, du, hd, 0, N), du, hd, f"alignment {res} ld {ld}")
+
+
+def test_repeated_runs_are_identical():
+    w, case = workload_case(3, "probe_cancel")
+    first = run_steps(case, w.P, 0, w.T, g.SDM_GX_STEPS_FUSED)
+    for _ in range(3):
+        case.reset()
+        again = run_steps(case, w.P, 0, w.T, g.SDM_GX_STEPS_FUSED)
+        assert (again.view(np.uint32) == first.view(np.uint32)).all()
+
+
+# ---- errors reach the caller and launch nothing --------------------------------------------------------------------
+def test_errors_launch_nothing():
+    import torch
+    N, P, C, hd = 4, 2, 8, 8
+    x, dv, du = inputs.shape_inputs(N, C, hd, None, "normal", seed=9)
+    case = DeviceCase(x, dv, du, hd)
+    with pytest.raises(ValueError):
+        g.sdm_gx_gemm_ex(case.du, hd, case.x, case.dv, hd, N, 2, P, C, hd)           # ti >= N / P
+    with pytest.raises(ValueError):
+        g.sdm_gx_gemm_ex(case.du, hd, case.du, case.dv, hd, N, 0, P, C, hd)          # d_u overlaps x
+    host = torch.zeros(N * C * hd)
+    with pytest.raises(RuntimeError):                                               # a host pointer
+        g.sdm_gx_gemm_ex(host.data_ptr(), hd, case.x, case.dv, hd, N, 0, P, C, hd)
+    step = g.make_step(case.du.view(N, C, hd), case.x.view(N, C, C), case.dv.view(N, C, hd), P)
+    with pytest.raises(ValueError):
+        step(2)
+    with pytest.raises(ValueError):
+        g.sdm_gx_launch(step.prepared, 5)
+    bad = g.sdm_gx_launch_t()
+    with pytest.raises(ValueError):
+        g.sdm_gx_launch(bad, 0)
+    torch.cuda.synchronize()
+    assert (case.result().view(np.uint32) == du.view(np.uint32)).all()
+
+
+def test_kernel_attrs_report_no_scratch():
+    for key in (1, 2, 3, 4, 5):
+        w = inputs.WORKLOADS[key]
+        plan = g.sdm_gx_plan(w.N, w.C, w.hd)
+        attrs = g.sdm_gx_kernel_attrs(plan)
+        say(f"workload {key}: {plan} {attrs}")
+        assert attrs["scratch_bytes"] == 0
+        assert 0 < attrs["vgprs"] <= 512

@@ -20,8 +20,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
-# FP32 FMA on the VALU without packed FP32: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.
-VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# FP32 vector peak, published (157.3 TFLOP/s): 256 CUs x 4 SIMDs x 32 FMA lanes per clock x 2 flop x 2.4 GHz. On
+# gfx950 plain VOP2 v_fmac_f32 with all-VGPR operands issues at this double rate (no packed FP32 needed); an SGPR
+# operand halves it.
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 METRIC = "GFLOP/s and HBM GB/s per gx_gemm step (fraction of roofline), bit-exact"
 KERNEL_SOURCES = ("deterministic_fp32_gemm_amd/csrc/gx_gemm_kernel.hip",)
 
@@ -34,14 +36,20 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key: int, driver: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the current kernel."""
+PLAN_KEYS = ("rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows")
+
+
+def measured_traffic(workload_key: int, driver: str, plan: dict):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled as the
+    copy calibration in profiles/ states), or None unless it was taken on the current kernel source and plan."""
     path = os.path.join(ROOT, "profiles", f"traffic_gx_chain_kernel_workload{workload_key}_{driver}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("kernel_sha256_16") != kernel_hash():
+        return None
+    if any(d.get("plan", {}).get(k) != plan.get(k) for k in PLAN_KEYS):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -207,7 +215,7 @@ def main():
         roof = {"bound": "alu", "achieved": flops_per_pass / launches_per_pass / launch_s / 1e12,
                 "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.key, args.driver)
+    roof["traffic"] = measured_traffic(w.key, args.driver, step.geom["fused" if args.driver == "fused" else "step"])
     roof["kernel"] = "gx_chain_kernel"
     roof["algorithmic_bytes_per_launch"] = bytes_per_launch
     roof["algorithmic_flops_per_launch"] = flops_per_pass / launches_per_pass

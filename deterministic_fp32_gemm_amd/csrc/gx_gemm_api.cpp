@@ -149,10 +149,13 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
     return SDM_GX_OK;
 }
 
-// The planner. Columns per lane: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
-// Rows per wavefront: as many as keep the grid at >= 4 wavefronts per CU (latency hiding), between 4 and the
-// register budget (RI*RC <= 64 accumulators); never more than C. Workgroups of up to 4 wavefronts share a chunk's
-// column block.
+// The planner (rules fitted to timing sweeps of every plan on MI355X; the choice never changes results).
+//  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
+//  * Rows per wavefront RI: 8 (with two x batches of U*RI scalars in flight), halved to 4 while the grid would hold
+//    fewer than 16 wavefronts per CU (small steps are latency-bound: more, shorter chains overlap better); never
+//    more than C.
+//  * 8 wavefronts per workgroup (fewer when the chunk has fewer row blocks), sharing the chunk's d_dv column block
+//    through an LDS slab (32 KiB), and the XCD-grouped workgroup order.
 int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out) {
     if (!out) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
@@ -166,23 +169,25 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             rc = cand;
         }
     }
-    const int ri_cap = rc == 1 ? 32 : (rc == 2 ? 32 : 16);
     int ri = 1;
-    while (ri * 2 <= ri_cap && ri * 2 <= C) ri *= 2;
+    while (ri * 2 <= 8 && ri * 2 <= C) ri *= 2;
     const int64_t ncb = cdiv(hd, 64 * rc);
-    const int64_t target_waves = 4LL * num_cus;
-    while (ri > 4 && nchunks * cdiv(C, ri) * ncb < target_waves) ri /= 2;
+    if (ri == 8 && nchunks * cdiv(C, ri) * ncb < 16LL * num_cus) ri = 4;
     const int64_t nrb = cdiv(C, ri);
     int waves = 1;
-    while (waves * 2 <= 4 && waves * 2 <= nrb) waves *= 2;
+    while (waves * 2 <= 8 && waves * 2 <= nrb) waves *= 2;
     sdm_gx_plan_t p{};
     p.rows_per_wave = ri;
     p.cols_per_lane = rc;
     p.waves_per_wg = waves;
-    p.staging = 0;
-    p.xcd_remap = 0;
+    p.staging = 1;
+    p.xcd_remap = 1;
     p.slab_rows = 0;
     int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+    if (st == SDM_GX_ERR_LIMIT) {               // a device with less LDS per workgroup: read d_dv directly
+        p.staging = 0;
+        st = complete_plan(&p, nchunks, C, hd, lds_limit);
+    }
     if (st) return st;
     *out = p;
     return SDM_GX_OK;

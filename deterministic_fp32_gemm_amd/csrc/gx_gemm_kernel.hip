@@ -32,7 +32,7 @@ namespace sdm_gx {
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4a __attribute__((ext_vector_type(4), aligned(16)));
-typedef __attribute__((address_space(4))) const float* cf32p;
+typedef __attribute__((address_space(4))) const float* cf32p;   // x: read-only, wave-uniform: scalar loads
 
 // RC adjacent floats of one row from global memory. FULL: all RC columns are < hd (one vector load, 4-byte aligned
 // is enough); otherwise per column, zero past hd (the pointer is only dereferenced for columns < hd).
@@ -54,35 +54,159 @@ __device__ __forceinline__ void load_cols(const float* row, int c, int hd, float
     }
 }
 
-// One step j of the chain for the wavefront's RI rows: acc[r][q] = fma(x[n, j, i0+r], d[q], acc[r][q]).
-// xrow points at x[n, j, i0] in the constant address space (wave-uniform address: scalar loads).
-template <int RI, int RC>
-__device__ __forceinline__ void chain_step(float (&acc)[RI][RC], cf32p xrow, const float (&d)[RC]) {
+// Rows of the chain per software-pipeline batch. Two batches of x live in SGPRs at once (the one being consumed and
+// the one in flight), so a batch holds at most 16 scalars (U*RI <= 16, U <= 4); RI = 32 rows would need 64 SGPRs
+// for two batches, so that tile runs one row at a time without the second register set.
+template <int RI>
+struct Batch {
+    static constexpr int U = RI >= 16 ? 1 : (RI == 8 ? 2 : 4);
+    static constexpr bool PIPE = RI <= 16;
+};
+
+// Wait until every scalar (and LDS) load issued so far has landed: s_waitcnt lgkmcnt(0), vmcnt/expcnt untouched.
+// Scalar loads return out of order, so this is the only way to wait for one batch; issuing the next batch only
+// after this wait keeps exactly one batch of x loads in flight while the previous one is consumed.
+__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Loads through the constant address space count as invariant, so the compiler may hoist them anywhere. Routing the
+// row index of the next batch through an empty volatile asm placed after the wait pins those loads behind it.
+__device__ __forceinline__ int after_wait(int j) {
+    asm volatile("" : "+s"(j));
+    return j;
+}
+
+// x[n, j, i0 .. i0+RI-1] for U consecutive rows j (wave-uniform addresses: scalar loads into SGPRs).
+template <int RI, int U>
+__device__ __forceinline__ void load_x(float (&xv)[U][RI], cf32p xr, int C, int j) {
 #pragma unroll
-    for (int r = 0; r < RI; ++r) {
-        const float xv = xrow[r];
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int q = 0; q < RC; ++q) acc[r][q] = __builtin_fmaf(xv, d[q], acc[r][q]);
+        for (int r = 0; r < RI; ++r) xv[u][r] = xr[(j + u) * C + r];
+}
+
+// The step's scalar x values copied into VGPRs. gfx950 issues v_fmac_f32 at twice the rate when every operand is a
+// VGPR but only at the base rate with an SGPR operand, so one v_mov_b32 per x value and step pays for itself as soon
+// as the value feeds two or more FMAs (RC >= 2). The copies are grouped four to a statement so that they land in
+// distinct registers ahead of the FMAs that read them.
+template <int RI>
+__device__ __forceinline__ void to_vgprs(const float (&s)[RI], float (&v)[RI]) {
+    if constexpr (RI % 4 == 0) {
+#pragma unroll
+        for (int r = 0; r < RI; r += 4)
+            asm("v_mov_b32 %0, %4\n\tv_mov_b32 %1, %5\n\tv_mov_b32 %2, %6\n\tv_mov_b32 %3, %7"
+                : "=&v"(v[r]), "=&v"(v[r + 1]), "=&v"(v[r + 2]), "=&v"(v[r + 3])
+                : "s"(s[r]), "s"(s[r + 1]), "s"(s[r + 2]), "s"(s[r + 3]));
+    } else {
+#pragma unroll
+        for (int r = 0; r < RI; ++r) asm("v_mov_b32 %0, %1" : "=v"(v[r]) : "s"(s[r]));
     }
 }
 
-// The whole chain j = 0 .. C-1 with d_dv read from global memory, U rows of d_dv loaded per batch.
-template <int RI, int RC, bool FULL>
-__device__ __forceinline__ void chain_direct(float (&acc)[RI][RC], cf32p xr, int C, const float* dvn, int64_t ld,
-                                             int c, int hd) {
-    constexpr int U = 4;
-    int j = 0;
-    for (; j + U <= C; j += U) {
-        float d[U][RC];
+// One step j of the chain for the wavefront's RI rows: acc[r][q] = fma(x[n, j, i0+r], d[q], acc[r][q]).
+template <int RI, int RC>
+__device__ __forceinline__ void chain_step(float (&acc)[RI][RC], const float (&xv)[RI], const float (&d)[RC]) {
+    if constexpr (RC >= 2) {
+        float xg[RI];
+        to_vgprs<RI>(xv, xg);
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_cols<RC, FULL>(dvn + static_cast<int64_t>(j + u) * ld, c, hd, d[u]);
+        for (int r = 0; r < RI; ++r)
 #pragma unroll
-        for (int u = 0; u < U; ++u) chain_step<RI, RC>(acc, xr + (j + u) * C, d[u]);
+            for (int q = 0; q < RC; ++q) acc[r][q] = __builtin_fmaf(xg[r], d[q], acc[r][q]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+            for (int q = 0; q < RC; ++q) acc[r][q] = __builtin_fmaf(xv[r], d[q], acc[r][q]);
     }
-    for (; j < C; ++j) {
-        float d[RC];
-        load_cols<RC, FULL>(dvn + static_cast<int64_t>(j) * ld, c, hd, d);
-        chain_step<RI, RC>(acc, xr + j * C, d);
+}
+
+// d_dv rows straight from global memory: row j of the chunk at base + j*ld, this lane's columns c .. c+RC-1.
+template <int RC, bool FULL>
+struct GlobalRows {
+    const float* base;
+    int64_t ld;
+    int c, hd;
+    __device__ __forceinline__ void load(float (&d)[RC], int j) const {
+        load_cols<RC, FULL>(base + static_cast<int64_t>(j) * ld, c, hd, d);
+    }
+};
+
+// d_dv rows from an LDS slab: slab row jj at base + jj*CW (base already offset by this lane's columns).
+template <int RC, int CW>
+struct LdsRows {
+    const float* base;
+    int first;       // chain row of slab row 0
+    __device__ __forceinline__ void load(float (&d)[RC], int j) const {
+        const float* p = base + (j - first) * CW;
+        if constexpr (RC == 4) {
+            const f32x4a v = *reinterpret_cast<const f32x4a*>(p);
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        } else if constexpr (RC == 2) {
+            d[0] = p[0]; d[1] = p[1];
+        } else {
+            d[0] = p[0];
+        }
+    }
+};
+
+template <int RI, int RC, int U, class Src>
+__device__ __forceinline__ void load_batch(float (&xv)[U][RI], float (&d)[U][RC], cf32p xr, int C, const Src& src,
+                                           int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) src.load(d[u], j + u);
+    load_x<RI, U>(xv, xr, C, j);
+}
+
+template <int RI, int RC, int U>
+__device__ __forceinline__ void compute_batch(float (&acc)[RI][RC], const float (&xv)[U][RI],
+                                              const float (&d)[U][RC]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) chain_step<RI, RC>(acc, xv[u], d[u]);
+}
+
+// The chain over rows j = j0 .. j1-1 in order. Batches of U rows are software-pipelined: batch b+1's x (scalar) and
+// d_dv loads are issued before batch b is computed, in two register sets used alternately.
+template <int RI, int RC, class Src>
+__device__ __forceinline__ void chain_rows(float (&acc)[RI][RC], cf32p xr, int C, int j0, int j1, const Src& src) {
+    constexpr int U = Batch<RI>::U;
+    if constexpr (!Batch<RI>::PIPE) {
+        for (int j = j0; j < j1; ++j) {
+            float xv[1][RI], d[1][RC];
+            load_batch<RI, RC, 1>(xv, d, xr, C, src, j);
+            chain_step<RI, RC>(acc, xv[0], d[0]);
+        }
+        return;
+    }
+    const int nb = (j1 - j0) / U;
+    float xa[U][RI], xb[U][RI];
+    float da[U][RC], db[U][RC];
+    int b = 0;
+    if (nb > 0) load_batch<RI, RC, U>(xa, da, xr, C, src, j0);
+    const int last = j0 + (nb - 1) * U;                 // first row of the last full batch
+    // sched_barrier(0) fences keep the order wait -> issue next batch -> compute current batch in the final code.
+    for (; b + 2 <= nb; b += 2) {
+        wait_scalar_loads();
+        load_batch<RI, RC, U>(xb, db, xr, C, src, after_wait(j0 + (b + 1) * U));
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch<RI, RC, U>(acc, xa, da);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_scalar_loads();
+        // the batch after next, clamped to the last full batch (a redundant in-range load at the end of the chain
+        // instead of a branch, so that the compiler keeps exactly two register sets)
+        const int jn = j0 + (b + 2) * U;
+        load_batch<RI, RC, U>(xa, da, xr, C, src, after_wait(jn < last ? jn : last));
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch<RI, RC, U>(acc, xb, db);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (b < nb) {
+        wait_scalar_loads();
+        compute_batch<RI, RC, U>(acc, xa, da);
+    }
+    for (int j = j0 + nb * U; j < j1; ++j) {      // the last (j1 - j0) % U rows
+        float xv[1][RI], d[1][RC];
+        load_batch<RI, RC, 1>(xv, d, xr, C, src, j);
+        chain_step<RI, RC>(acc, xv[0], d[0]);
     }
 }
 
@@ -150,10 +274,10 @@ __global__ __launch_bounds__(64 * WAVES) void gx_chain_kernel(const KernelArgs a
     if constexpr (STAGE == 0) {
         if (!active) return;                                      // no barrier in this variant
         if (full) {
-            chain_direct<RI, RC, true>(acc, xr, C, dvn, a.ld_dv, c, hd);
+            chain_rows<RI, RC>(acc, xr, C, 0, C, GlobalRows<RC, true>{dvn, a.ld_dv, c, hd});
             store_rows<RI, RC, true>(acc, dun, a.ld_u, i0, i_own, c, hd);
         } else {
-            chain_direct<RI, RC, false>(acc, xr, C, dvn, a.ld_dv, c, hd);
+            chain_rows<RI, RC>(acc, xr, C, 0, C, GlobalRows<RC, false>{dvn, a.ld_dv, c, hd});
             store_rows<RI, RC, false>(acc, dun, a.ld_u, i0, i_own, c, hd);
         }
     } else {
@@ -182,21 +306,7 @@ __global__ __launch_bounds__(64 * WAVES) void gx_chain_kernel(const KernelArgs a
                 *reinterpret_cast<f32x4a*>(ds + rr * CW + cc) = v;
             }
             __syncthreads();                                      // the slab is in LDS
-            if (active) {
-                for (int jj = 0; jj < rows; ++jj) {
-                    float d[RC];
-                    const float* src = ds + jj * CW + lane * RC;
-                    if constexpr (RC == 4) {
-                        const f32x4a v = *reinterpret_cast<const f32x4a*>(src);
-                        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-                    } else if constexpr (RC == 2) {
-                        d[0] = src[0]; d[1] = src[1];
-                    } else {
-                        d[0] = src[0];
-                    }
-                    chain_step<RI, RC>(acc, xr + (s + jj) * C, d);
-                }
-            }
+            if (active) chain_rows<RI, RC>(acc, xr, C, s, s + rows, LdsRows<RC, CW>{ds + lane * RC, s});
         }
         if (active) {
             if (full) store_rows<RI, RC, true>(acc, dun, a.ld_u, i0, i_own, c, hd);

@@ -114,9 +114,9 @@ int on_device(const void* p, int dev) {
 // ---- planner ------------------------------------------------------------------------------------------------------
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool valid_ri(int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16 || v == 32; }
+bool valid_ri(int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16; }
 bool valid_rc(int v) { return v == 1 || v == 2 || v == 4; }
-bool valid_waves(int v) { return v == 1 || v == 2 || v == 4 || v == 8; }
+bool valid_waves(int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16; }
 
 constexpr int kDefaultSlabBytes = 32 * 1024;
 
@@ -134,7 +134,6 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
         int64_t sj = p->slab_rows;
         if (sj == 0) sj = kDefaultSlabBytes / (cw * 4);
         if (sj > C) sj = C;
-        if (sj < 1) sj = 1;
         p->slab_rows = static_cast<int32_t>(sj);
         p->lds_bytes = static_cast<int32_t>(sj * cw * 4);
         if (lds_limit > 0 && p->lds_bytes > lds_limit) return SDM_GX_ERR_LIMIT;
@@ -149,13 +148,16 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
     return SDM_GX_OK;
 }
 
-// The planner (rules fitted to timing sweeps of every plan on MI355X; the choice never changes results).
+// The planner (rules fitted to interleaved timing sweeps of every plan on MI355X; the choice never changes results).
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
-//  * Rows per wavefront RI: 8 (with two x batches of U*RI scalars in flight), halved to 4 while the grid would hold
-//    fewer than 16 wavefronts per CU (small steps are latency-bound: more, shorter chains overlap better); never
-//    more than C.
-//  * 8 wavefronts per workgroup (fewer when the chunk has fewer row blocks), sharing the chunk's d_dv column block
-//    through an LDS slab (32 KiB), and the XCD-grouped workgroup order.
+//  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
+//    hold fewer than 8 wavefronts per CU (small steps are latency-bound: more, shorter tiles overlap better);
+//    never more than C.
+//  * 8 wavefronts per workgroup (fewer when the chunk has fewer row blocks, or when fewer would spread the grid
+//    over more CUs: at least one workgroup per CU).
+//  * RC <= 2: the workgroup stages d_dv through a 32 KiB LDS slab, with the XCD-grouped workgroup order.
+//    RC = 4: each wavefront reads d_dv straight from global memory (64 columns of 16 bytes per row: the LDS round
+//    trip measured slower there).
 int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out) {
     if (!out) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
@@ -172,16 +174,17 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
     int ri = 1;
     while (ri * 2 <= 8 && ri * 2 <= C) ri *= 2;
     const int64_t ncb = cdiv(hd, 64 * rc);
-    if (ri == 8 && nchunks * cdiv(C, ri) * ncb < 16LL * num_cus) ri = 4;
+    while (ri > 4 && nchunks * cdiv(C, ri) * ncb < 8LL * num_cus) ri /= 2;
     const int64_t nrb = cdiv(C, ri);
     int waves = 1;
     while (waves * 2 <= 8 && waves * 2 <= nrb) waves *= 2;
+    while (waves > 1 && nchunks * cdiv(nrb, waves) * ncb < num_cus) waves /= 2;   // at least one workgroup per CU
     sdm_gx_plan_t p{};
     p.rows_per_wave = ri;
     p.cols_per_lane = rc;
     p.waves_per_wg = waves;
-    p.staging = 1;
-    p.xcd_remap = 1;
+    p.staging = rc <= 2 ? 1 : 0;
+    p.xcd_remap = rc <= 2 ? 1 : 0;
     p.slab_rows = 0;
     int st = complete_plan(&p, nchunks, C, hd, lds_limit);
     if (st == SDM_GX_ERR_LIMIT) {               // a device with less LDS per workgroup: read d_dv directly

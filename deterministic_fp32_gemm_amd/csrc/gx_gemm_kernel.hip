@@ -27,6 +27,7 @@
 
 #include "gx_gemm_kernel.h"
 
+
 namespace sdm_gx {
 
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
@@ -54,13 +55,15 @@ __device__ __forceinline__ void load_cols(const float* row, int c, int hd, float
     }
 }
 
-// Rows of the chain per software-pipeline batch. Two batches of x live in SGPRs at once (the one being consumed and
-// the one in flight), so a batch holds at most 16 scalars (U*RI <= 16, U <= 4); RI = 32 rows would need 64 SGPRs
-// for two batches, so that tile runs one row at a time without the second register set.
-template <int RI>
+// Rows of the chain per software-pipeline batch. Two batches are live at once (the one being consumed and the one in
+// flight). Each batch costs one scalar-load round trip, so tiles with few rows per wavefront take long batches (up
+// to 16 rows) and few round trips per chain. Limits, found by checking the build for spills: U*RI <= 32 scalar x
+// values (16 for RI = 16), U*RC <= 16 d_dv values per lane, U <= 16.
+template <int RI, int RC>
 struct Batch {
-    static constexpr int U = RI >= 16 ? 1 : (RI == 8 ? 2 : 4);
-    static constexpr bool PIPE = RI <= 16;
+    static constexpr int BY_SGPR = (RI >= 16 ? 16 : 32) / RI, BY_VGPR = 16 / RC;
+    static constexpr int U0 = BY_SGPR < BY_VGPR ? BY_SGPR : BY_VGPR;
+    static constexpr int U = U0 < 1 ? 1 : (U0 > 16 ? 16 : U0);
 };
 
 // Wait until every scalar (and LDS) load issued so far has landed: s_waitcnt lgkmcnt(0), vmcnt/expcnt untouched.
@@ -85,17 +88,21 @@ __device__ __forceinline__ void load_x(float (&xv)[U][RI], cf32p xr, int C, int 
 }
 
 // The step's scalar x values copied into VGPRs. gfx950 issues v_fmac_f32 at twice the rate when every operand is a
-// VGPR but only at the base rate with an SGPR operand, so one v_mov_b32 per x value and step pays for itself as soon
-// as the value feeds two or more FMAs (RC >= 2). The copies are grouped four to a statement so that they land in
-// distinct registers ahead of the FMAs that read them.
+// VGPR but only at the base rate with an SGPR operand, so copying each x value once per step (v_mov_b64 moves an
+// adjacent pair from an SGPR pair) pays for itself as soon as the value feeds two or more FMAs (RC >= 2). Measured on
+// the RC = 2 pattern: 100 TFLOP/s with pair copies, 90 with single copies, 75 with the SGPR operand. The copies are
+// grouped two pairs to a statement so that they land in distinct registers ahead of the FMAs that read them.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int RI>
 __device__ __forceinline__ void to_vgprs(const float (&s)[RI], float (&v)[RI]) {
     if constexpr (RI % 4 == 0) {
 #pragma unroll
-        for (int r = 0; r < RI; r += 4)
-            asm("v_mov_b32 %0, %4\n\tv_mov_b32 %1, %5\n\tv_mov_b32 %2, %6\n\tv_mov_b32 %3, %7"
-                : "=&v"(v[r]), "=&v"(v[r + 1]), "=&v"(v[r + 2]), "=&v"(v[r + 3])
-                : "s"(s[r]), "s"(s[r + 1]), "s"(s[r + 2]), "s"(s[r + 3]));
+        for (int r = 0; r < RI; r += 4) {
+            f32x2 a, b;
+            const f32x2 sa = {s[r], s[r + 1]}, sb = {s[r + 2], s[r + 3]};
+            asm("v_mov_b64 %0, %2\n\tv_mov_b64 %1, %3" : "=&v"(a), "=&v"(b) : "s"(sa), "s"(sb));
+            v[r] = a.x; v[r + 1] = a.y; v[r + 2] = b.x; v[r + 3] = b.y;
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < RI; ++r) asm("v_mov_b32 %0, %1" : "=v"(v[r]) : "s"(s[r]));
@@ -168,38 +175,34 @@ __device__ __forceinline__ void compute_batch(float (&acc)[RI][RC], const float 
 // d_dv loads are issued before batch b is computed, in two register sets used alternately.
 template <int RI, int RC, class Src>
 __device__ __forceinline__ void chain_rows(float (&acc)[RI][RC], cf32p xr, int C, int j0, int j1, const Src& src) {
-    constexpr int U = Batch<RI>::U;
-    if constexpr (!Batch<RI>::PIPE) {
-        for (int j = j0; j < j1; ++j) {
-            float xv[1][RI], d[1][RC];
-            load_batch<RI, RC, 1>(xv, d, xr, C, src, j);
-            chain_step<RI, RC>(acc, xv[0], d[0]);
-        }
-        return;
-    }
+    constexpr int U = Batch<RI, RC>::U;
     const int nb = (j1 - j0) / U;
     float xa[U][RI], xb[U][RI];
     float da[U][RC], db[U][RC];
     int b = 0;
     if (nb > 0) load_batch<RI, RC, U>(xa, da, xr, C, src, j0);
-    const int last = j0 + (nb - 1) * U;                 // first row of the last full batch
     // sched_barrier(0) fences keep the order wait -> issue next batch -> compute current batch in the final code.
-    for (; b + 2 <= nb; b += 2) {
+    for (; b + 2 < nb; b += 2) {                      // batches b, b+1 computed; b+1 and b+2 issued
         wait_scalar_loads();
         load_batch<RI, RC, U>(xb, db, xr, C, src, after_wait(j0 + (b + 1) * U));
         __builtin_amdgcn_sched_barrier(0);
         compute_batch<RI, RC, U>(acc, xa, da);
         __builtin_amdgcn_sched_barrier(0);
         wait_scalar_loads();
-        // the batch after next, clamped to the last full batch (a redundant in-range load at the end of the chain
-        // instead of a branch, so that the compiler keeps exactly two register sets)
-        const int jn = j0 + (b + 2) * U;
-        load_batch<RI, RC, U>(xa, da, xr, C, src, after_wait(jn < last ? jn : last));
+        load_batch<RI, RC, U>(xa, da, xr, C, src, after_wait(j0 + (b + 2) * U));
         __builtin_amdgcn_sched_barrier(0);
         compute_batch<RI, RC, U>(acc, xb, db);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (b < nb) {
+    if (b + 2 == nb) {                                // the last two batches: one more to issue
+        wait_scalar_loads();
+        load_batch<RI, RC, U>(xb, db, xr, C, src, after_wait(j0 + (b + 1) * U));
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch<RI, RC, U>(acc, xa, da);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_scalar_loads();
+        compute_batch<RI, RC, U>(acc, xb, db);
+    } else if (b + 1 == nb) {                         // the last batch, already issued
         wait_scalar_loads();
         compute_batch<RI, RC, U>(acc, xa, da);
     }
@@ -210,30 +213,41 @@ __device__ __forceinline__ void chain_rows(float (&acc)[RI][RC], cf32p xr, int C
     }
 }
 
-// d_u[n, i0+r, c+q] = d_u[n, i0+r, c+q] + acc[r][q] for the rows this wavefront owns (i >= i_own) and columns < hd.
+// d_u[n, i0+r, c .. c+RC-1] for the rows this wavefront owns (i >= i_own), read after the chain (reading it earlier
+// costs registers, and occupancy, for no measured gain); columns >= hd are neither read nor written.
 template <int RI, int RC, bool FULL>
-__device__ __forceinline__ void store_rows(const float (&acc)[RI][RC], float* dun, int64_t ld, int i0, int i_own,
-                                           int c, int hd) {
+__device__ __forceinline__ void load_rows(float (&u)[RI][RC], const float* dun, int64_t ld, int i0, int i_own, int c,
+                                          int hd) {
+    const float* row = dun + static_cast<int64_t>(i0) * ld;
 #pragma unroll
-    for (int r = 0; r < RI; ++r) {
+    for (int r = 0; r < RI; ++r, row += ld) {
+#pragma unroll
+        for (int q = 0; q < RC; ++q) u[r][q] = 0.0f;
+        if (i0 + r >= i_own) load_cols<RC, FULL>(row, c, hd, u[r]);   // wave-uniform: rows this wavefront owns
+    }
+}
+
+// d_u[n, i0+r, c+q] = u[r][q] + acc[r][q] (one rounding) for the owned rows and columns < hd.
+template <int RI, int RC, bool FULL>
+__device__ __forceinline__ void store_rows(const float (&acc)[RI][RC], const float (&u)[RI][RC], float* dun, int64_t ld,
+                                           int i0, int i_own, int c, int hd) {
+    float* row = dun + static_cast<int64_t>(i0) * ld;
+#pragma unroll
+    for (int r = 0; r < RI; ++r, row += ld) {
         if (i0 + r < i_own) continue;                       // wave-uniform: rows of the previous row block
-        float* row = dun + static_cast<int64_t>(i0 + r) * ld;
         if constexpr (FULL) {
             if constexpr (RC == 4) {
-                f32x4u u = *reinterpret_cast<const f32x4u*>(row + c);
-                u.x = u.x + acc[r][0]; u.y = u.y + acc[r][1]; u.z = u.z + acc[r][2]; u.w = u.w + acc[r][3];
-                *reinterpret_cast<f32x4u*>(row + c) = u;
+                *reinterpret_cast<f32x4u*>(row + c) =
+                    f32x4u{u[r][0] + acc[r][0], u[r][1] + acc[r][1], u[r][2] + acc[r][2], u[r][3] + acc[r][3]};
             } else if constexpr (RC == 2) {
-                f32x2u u = *reinterpret_cast<const f32x2u*>(row + c);
-                u.x = u.x + acc[r][0]; u.y = u.y + acc[r][1];
-                *reinterpret_cast<f32x2u*>(row + c) = u;
+                *reinterpret_cast<f32x2u*>(row + c) = f32x2u{u[r][0] + acc[r][0], u[r][1] + acc[r][1]};
             } else {
-                row[c] = row[c] + acc[r][0];
+                row[c] = u[r][0] + acc[r][0];
             }
         } else {
 #pragma unroll
             for (int q = 0; q < RC; ++q)
-                if (c + q < hd) row[c + q] = row[c + q] + acc[r][q];
+                if (c + q < hd) row[c + q] = u[r][q] + acc[r][q];
         }
     }
 }
@@ -271,14 +285,18 @@ __global__ __launch_bounds__(64 * WAVES) void gx_chain_kernel(const KernelArgs a
 #pragma unroll
         for (int q = 0; q < RC; ++q) acc[r][q] = 0.0f;              // the chain starts from +0
 
+    float u[RI][RC];
+
     if constexpr (STAGE == 0) {
         if (!active) return;                                      // no barrier in this variant
         if (full) {
             chain_rows<RI, RC>(acc, xr, C, 0, C, GlobalRows<RC, true>{dvn, a.ld_dv, c, hd});
-            store_rows<RI, RC, true>(acc, dun, a.ld_u, i0, i_own, c, hd);
+            load_rows<RI, RC, true>(u, dun, a.ld_u, i0, i_own, c, hd);
+            store_rows<RI, RC, true>(acc, u, dun, a.ld_u, i0, i_own, c, hd);
         } else {
             chain_rows<RI, RC>(acc, xr, C, 0, C, GlobalRows<RC, false>{dvn, a.ld_dv, c, hd});
-            store_rows<RI, RC, false>(acc, dun, a.ld_u, i0, i_own, c, hd);
+            load_rows<RI, RC, false>(u, dun, a.ld_u, i0, i_own, c, hd);
+            store_rows<RI, RC, false>(acc, u, dun, a.ld_u, i0, i_own, c, hd);
         }
     } else {
         // d_dv slab [SJ][CW] in LDS, rows s .. s+SJ-1, columns c0 .. c0+CW-1 (zero past hd).
@@ -309,19 +327,28 @@ __global__ __launch_bounds__(64 * WAVES) void gx_chain_kernel(const KernelArgs a
             if (active) chain_rows<RI, RC>(acc, xr, C, s, s + rows, LdsRows<RC, CW>{ds + lane * RC, s});
         }
         if (active) {
-            if (full) store_rows<RI, RC, true>(acc, dun, a.ld_u, i0, i_own, c, hd);
-            else store_rows<RI, RC, false>(acc, dun, a.ld_u, i0, i_own, c, hd);
+            if (full) {
+                load_rows<RI, RC, true>(u, dun, a.ld_u, i0, i_own, c, hd);
+                store_rows<RI, RC, true>(acc, u, dun, a.ld_u, i0, i_own, c, hd);
+            } else {
+                load_rows<RI, RC, false>(u, dun, a.ld_u, i0, i_own, c, hd);
+                store_rows<RI, RC, false>(acc, u, dun, a.ld_u, i0, i_own, c, hd);
+            }
         }
     }
 }
 
 // ---- instance table -----------------------------------------------------------------------------------------------
+// Instances: every (RI, RC) tile for 1, 2, 4 and 8 wavefronts per workgroup; 16 wavefronts (1024 threads, so at
+// most 128 VGPRs per lane) only for the tiles that fit without spilling.
 #define SDM_GX_INST(RI, RC, W, S) {RI, RC, W, S, reinterpret_cast<const void*>(&gx_chain_kernel<RI, RC, W, S>)},
 #define SDM_GX_INST_W(RI, RC, S) SDM_GX_INST(RI, RC, 1, S) SDM_GX_INST(RI, RC, 2, S) SDM_GX_INST(RI, RC, 4, S) \
     SDM_GX_INST(RI, RC, 8, S)
 #define SDM_GX_INST_RC(RI, S) SDM_GX_INST_W(RI, 1, S) SDM_GX_INST_W(RI, 2, S) SDM_GX_INST_W(RI, 4, S)
 #define SDM_GX_INST_S(S) SDM_GX_INST_RC(1, S) SDM_GX_INST_RC(2, S) SDM_GX_INST_RC(4, S) SDM_GX_INST_RC(8, S) \
-    SDM_GX_INST_RC(16, S) SDM_GX_INST_W(32, 1, S) SDM_GX_INST_W(32, 2, S)
+    SDM_GX_INST_RC(16, S) \
+    SDM_GX_INST(4, 1, 16, S) SDM_GX_INST(4, 2, 16, S) SDM_GX_INST(4, 4, 16, S) SDM_GX_INST(8, 1, 16, S) \
+    SDM_GX_INST(8, 2, 16, S) SDM_GX_INST(8, 4, 16, S) SDM_GX_INST(16, 1, 16, S)
 
 static const KernelEntry kTable[] = {SDM_GX_INST_S(0) SDM_GX_INST_S(1)};
 

@@ -74,10 +74,10 @@ typedef enum sdm_gx_status {
 } sdm_gx_status;
 
 /* A launch plan: how output tiles map onto wavefronts and workgroups. Results never depend on it.
- *   rows_per_wave  RI: output rows one wavefront owns (1, 2, 4, 8, 16 or 32; RI <= C)
+ *   rows_per_wave  RI: output rows one wavefront owns (1, 2, 4, 8 or 16; RI <= C)
  *   cols_per_lane  RC: adjacent output columns one lane owns (1, 2 or 4); a wavefront covers 64*RC columns
- *   waves_per_wg   wavefronts per workgroup (1, 2, 4 or 8); they take consecutive row blocks of one chunk and
- *                  column block
+ *   waves_per_wg   wavefronts per workgroup (1, 2, 4, 8, or 16 for some tiles); they take consecutive row blocks of
+ *                  one chunk and column block
  *   staging        0: each wavefront reads its d_dv columns straight from global memory;
  *                  1: the workgroup stages its d_dv column block in LDS once and every wavefront reads it there
  *   xcd_remap      1: workgroup ids are permuted so that the workgroups of one chunk run on one XCD (one L2)

@@ -126,7 +126,7 @@ def test_plan_for_emits_supported_plans():
     for nchunks in (0, 1, 7, 128, 4096):
         for C, hd in shapes:
             p = g.sdm_gx_plan_for(nchunks, C, hd)
-            assert p.rows_per_wave in (1, 2, 4, 8, 16, 32) and p.rows_per_wave <= C
+            assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
             assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
             assert p.waves_per_wg in (1, 2, 4, 8)
             nrb = -(-C // p.rows_per_wave)
@@ -138,8 +138,8 @@ def test_plan_for_emits_supported_plans():
 
 @pytest.mark.parametrize("bad", [
     dict(rows_per_wave=3), dict(rows_per_wave=64), dict(cols_per_lane=3), dict(waves_per_wg=3),
-    dict(waves_per_wg=16), dict(staging=2), dict(xcd_remap=2), dict(slab_rows=-1),
-    dict(rows_per_wave=32, cols_per_lane=4),
+    dict(waves_per_wg=32), dict(staging=2), dict(xcd_remap=2), dict(slab_rows=-1),
+    dict(rows_per_wave=32), dict(rows_per_wave=16, cols_per_lane=4, waves_per_wg=16),
 ])
 def test_plan_complete_rejects(bad):
     p = g.make_plan(8, 1, 4)

@@ -83,19 +83,23 @@ def test_workload_bench_launch(key):
 
 
 # ---- every plan gives the same bits --------------------------------------------------------------------------------
-def all_plans(C):
+def all_plans(C, hd=64):
+    """Every plan the library has a kernel instance for (plans without one are rejected by the library)."""
     for ri in (1, 2, 4, 8, 16, 32):
         if ri > C:
             continue
         for rc in (1, 2, 4):
-            if ri * rc > 64:
-                continue
-            for waves in (1, 2, 4, 8):
+            for waves in (1, 2, 4, 8, 16):
                 for staging in (0, 1):
                     for xcd in (0, 1):
                         slab = (0, 5) if staging else (0,)
                         for sj in slab:
-                            yield g.make_plan(ri, rc, waves, staging, xcd, sj)
+                            plan = g.make_plan(ri, rc, waves, staging, xcd, sj)
+                            try:
+                                g.sdm_gx_plan_complete(plan, 1, C, hd)
+                            except ValueError:
+                                continue
+                            yield plan
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8)])
@@ -220,6 +224,20 @@ def test_errors_launch_nothing():
         g.sdm_gx_launch(bad, 0)
     torch.cuda.synchronize()
     assert (case.result().view(np.uint32) == du.view(np.uint32)).all()
+
+
+def test_no_kernel_instance_spills():
+    """Every kernel instance runs without private (scratch) memory."""
+    seen = set()
+    for plan in all_plans(256, 4096):
+        key = (plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
+        if key in seen:
+            continue
+        seen.add(key)
+        attrs = g.sdm_gx_kernel_attrs(plan)
+        assert attrs["scratch_bytes"] == 0, (key, attrs)
+        assert attrs["vgprs"] * plan.waves_per_wg <= 512 * 4 or plan.waves_per_wg < 16, (key, attrs)
+    assert len(seen) > 100
 
 
 def test_kernel_attrs_report_no_scratch():

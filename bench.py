@@ -25,7 +25,7 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
 # operand halves it.
 VALU_FP32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 METRIC = "GFLOP/s and HBM GB/s per gx_gemm step (fraction of roofline), bit-exact"
-KERNEL_SOURCES = ("deterministic_fp32_gemm_amd/csrc/gx_gemm_kernel.hip",)
+KERNEL_SOURCES = ("deterministic_fp32_gemm_amd/csrc/gx_gemm_kernel.hip", "deterministic_fp32_gemm_amd/csrc/gx_gemm_mfma.hip")
 
 
 def kernel_hash() -> str:
@@ -36,13 +36,18 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-PLAN_KEYS = ("rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows")
+PLAN_KEYS = ("engine", "rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows",
+             "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups")
+
+
+def kernel_name(plan: dict) -> str:
+    return "gx_mfma_kernel" if plan.get("engine") == 1 else "gx_chain_kernel"
 
 
 def measured_traffic(workload_key: int, driver: str, plan: dict):
     """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled as the
     copy calibration in profiles/ states), or None unless it was taken on the current kernel source and plan."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gx_chain_kernel_workload{workload_key}_{driver}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name(plan)}_workload{workload_key}_{driver}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -64,7 +69,9 @@ def parse():
     ap.add_argument("--cold", action="store_true", help="flush the caches before every timed launch (adds a field)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--plan", default=None, help="override: RI,RC,WAVES,STAGING,XCD[,SLAB]")
+    ap.add_argument("--plan", default=None,
+                    help="override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,REG_SLABS,"
+                         "LOADER_WAVES[,WORKGROUPS]")
     return ap.parse_args()
 
 
@@ -101,8 +108,9 @@ def main():
     x3, dv3, du3 = x.view(N, C, C), dv.view(N, C, ld)[:, :, :hd], du.view(N, C, ld)[:, :, :hd]
     plan = None
     if args.plan:
-        f = [int(v) for v in args.plan.split(",")]
-        plan = g.make_plan(*f)
+        engine, _, fields = args.plan.partition(":")
+        f = [int(v) for v in fields.split(",")]
+        plan = g.make_mfma_plan(*f) if engine == "mfma" else g.make_plan(*f)
     step = g.make_step(du3, x3, dv3, P, plan)
     stream = torch.cuda.current_stream()
 
@@ -219,7 +227,7 @@ def main():
                 "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(w.key, args.driver, step.geom["fused" if args.driver == "fused" else "step"])
-    roof["kernel"] = "gx_chain_kernel"
+    roof["kernel"] = kernel_name(step.geom["fused" if args.driver == "fused" else "step"])
     roof["algorithmic_bytes_per_launch"] = bytes_per_launch
     roof["algorithmic_flops_per_launch"] = flops_per_pass / launches_per_pass
     roof["launch_ms_mean"] = launch_ms_mean

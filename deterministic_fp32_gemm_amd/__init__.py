@@ -8,6 +8,8 @@ include/sdm_gx_gemm.h; the functions below carry the same names and only marshal
 
 from ._binding import (  # noqa: F401
     EXPORTS,
+    SDM_GX_ENGINE_MFMA,
+    SDM_GX_ENGINE_VALU,
     SDM_GX_ERR_ALIGN,
     SDM_GX_ERR_ARG,
     SDM_GX_ERR_DEVICE,
@@ -24,6 +26,7 @@ from ._binding import (  # noqa: F401
     SDM_GX_STEPS_FUSED,
     SDM_GX_STEPS_REVERSE,
     load,
+    make_mfma_plan,
     make_plan,
     sdm_gx_abi_version,
     sdm_gx_check,

@@ -27,6 +27,9 @@ SDM_GX_ERR_PLAN = -9
 SDM_GX_ERR_DEVICE = -10
 SDM_GX_ERR_ARG = -11
 
+SDM_GX_ENGINE_VALU = 0
+SDM_GX_ENGINE_MFMA = 1
+
 SDM_GX_STEPS_FORWARD = 0
 SDM_GX_STEPS_REVERSE = 1
 SDM_GX_STEPS_FUSED = 2
@@ -36,9 +39,14 @@ _ARG_ERRORS = {SDM_GX_ERR_NULL, SDM_GX_ERR_SHAPE, SDM_GX_ERR_STEP, SDM_GX_ERR_AL
 
 
 class sdm_gx_plan_t(ctypes.Structure):
-    _fields_ = [("rows_per_wave", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
+    _fields_ = [("engine", ctypes.c_int32),
+                ("rows_per_wave", ctypes.c_int32), ("cols_per_lane", ctypes.c_int32),
                 ("waves_per_wg", ctypes.c_int32), ("staging", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("slab_rows", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
+                ("slab_rows", ctypes.c_int32),
+                ("mf_row_waves", ctypes.c_int32), ("mf_col_waves", ctypes.c_int32), ("mf_stages", ctypes.c_int32),
+                ("mf_reg_slabs", ctypes.c_int32), ("mf_loader_waves", ctypes.c_int32),
+                ("mf_workgroups", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
@@ -192,8 +200,21 @@ def sdm_gx_plan_for(nchunks, C, hd, num_cus=256, lds_per_cu=160 * 1024) -> sdm_g
 
 
 def make_plan(rows_per_wave, cols_per_lane, waves_per_wg, staging=0, xcd_remap=0, slab_rows=0) -> sdm_gx_plan_t:
-    """A caller-made plan (validated by the entry point that receives it)."""
-    return sdm_gx_plan_t(rows_per_wave, cols_per_lane, waves_per_wg, staging, xcd_remap, slab_rows, 0, 0, 0)
+    """A caller-made plan for the vector-ALU engine (validated by the entry point that receives it)."""
+    p = sdm_gx_plan_t()
+    p.engine = SDM_GX_ENGINE_VALU
+    p.rows_per_wave, p.cols_per_lane, p.waves_per_wg = rows_per_wave, cols_per_lane, waves_per_wg
+    p.staging, p.xcd_remap, p.slab_rows = staging, xcd_remap, slab_rows
+    return p
+
+
+def make_mfma_plan(row_waves, col_waves, stages=4, reg_slabs=4, loader_waves=4, workgroups=0) -> sdm_gx_plan_t:
+    """A caller-made plan for the matrix-core engine (validated by the entry point that receives it)."""
+    p = sdm_gx_plan_t()
+    p.engine = SDM_GX_ENGINE_MFMA
+    p.mf_row_waves, p.mf_col_waves, p.mf_stages = row_waves, col_waves, stages
+    p.mf_reg_slabs, p.mf_loader_waves, p.mf_workgroups = reg_slabs, loader_waves, workgroups
+    return p
 
 
 def sdm_gx_plan_complete(plan: sdm_gx_plan_t, nchunks, C, hd, lds_per_cu=160 * 1024) -> sdm_gx_plan_t:

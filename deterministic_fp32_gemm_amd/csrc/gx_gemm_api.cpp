@@ -1,6 +1,6 @@
 // Host entry points of libsdm_gx_gemm: argument checks, the launch planner, single-step, multi-step and prepared
 // launches. Everything that decides whether and how to launch runs here; every arithmetic step of the update runs
-// in the kernels of gx_gemm_kernel.hip.
+// in the kernels of gx_gemm_kernel.hip (vector-ALU engine) and gx_gemm_mfma.hip (matrix-core engine).
 //
 // The checks follow the page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py": the host entry
 // gx_gemm (shape, step range, overlap and alignment checks) and supported(); the prepared launch follows its
@@ -14,6 +14,7 @@
 
 #include "../../include/sdm_gx_gemm.h"
 #include "gx_gemm_kernel.h"
+#include "gx_gemm_mfma.h"
 
 namespace {
 
@@ -120,15 +121,46 @@ bool valid_waves(int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16
 
 constexpr int kDefaultSlabBytes = 32 * 1024;
 
+constexpr int kDefaultCus = 256;                // MI355X
+
+// Geometry of the matrix-core engine for nchunks chunks: work items and the persistent grid.
+struct MfmaGeom {
+    int64_t nrg, ncg, items, per, grid;
+};
+MfmaGeom mfma_geom(const sdm_gx_plan_t& p, int64_t nchunks, int64_t C, int64_t hd) {
+    MfmaGeom g;
+    g.nrg = cdiv(cdiv(C, 64), p.mf_row_waves);
+    g.ncg = cdiv(hd, 32 * p.mf_col_waves);
+    g.items = nchunks * g.nrg * g.ncg;
+    const int64_t wg = p.mf_workgroups > 0 ? p.mf_workgroups : kDefaultCus;
+    const int64_t g0 = g.items < wg ? g.items : wg;
+    g.per = g0 > 0 ? cdiv(g.items, g0) : 0;
+    g.grid = g.per > 0 ? cdiv(g.items, g.per) : 0;
+    return g;
+}
+
 // Fill the derived fields of a plan and check it against the shape; lds_limit: max LDS bytes per workgroup.
 int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int64_t lds_limit) {
+    if (nchunks < 0) return SDM_GX_ERR_ARG;
+    if (p->engine == SDM_GX_ENGINE_MFMA) {
+        if (p->mf_workgroups < 0) return SDM_GX_ERR_PLAN;
+        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p->mf_row_waves, p->mf_col_waves, p->mf_stages,
+                                                             p->mf_reg_slabs, p->mf_loader_waves);
+        if (!e) return SDM_GX_ERR_PLAN;
+        p->lds_bytes = e->lds_bytes;
+        if (lds_limit > 0 && p->lds_bytes > lds_limit) return SDM_GX_ERR_LIMIT;
+        const MfmaGeom g = mfma_geom(*p, nchunks, C, hd);
+        if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;   // item indices are 32-bit in the kernel
+        p->grid = g.grid;
+        return SDM_GX_OK;
+    }
+    if (p->engine != SDM_GX_ENGINE_VALU) return SDM_GX_ERR_PLAN;
     if (!valid_ri(p->rows_per_wave) || !valid_rc(p->cols_per_lane) || !valid_waves(p->waves_per_wg))
         return SDM_GX_ERR_PLAN;
     if (p->staging != 0 && p->staging != 1) return SDM_GX_ERR_PLAN;
     if (p->xcd_remap != 0 && p->xcd_remap != 1) return SDM_GX_ERR_PLAN;
     if (p->rows_per_wave > C || p->slab_rows < 0) return SDM_GX_ERR_PLAN;
     if (!sdm_gx::find_kernel(p->rows_per_wave, p->cols_per_lane, p->waves_per_wg, p->staging)) return SDM_GX_ERR_PLAN;
-    if (nchunks < 0) return SDM_GX_ERR_ARG;
     const int64_t cw = 64 * p->cols_per_lane;
     if (p->staging == 1) {
         int64_t sj = p->slab_rows;
@@ -149,6 +181,13 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 }
 
 // The planner (rules fitted to interleaved timing sweeps of every plan on MI355X; the choice never changes results).
+// Engine: the matrix cores for chunks with 32 <= C and hd <= 128, where their streaming kernel measured fastest
+// (64x64, 64x128 and 128x128 chunks); the vector-ALU chain otherwise (narrow C, where 64-row MFMA tiles would be
+// mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
+//  Matrix cores: one work item per chunk when it is at most 128 x 128 (row waves ceil(C/64) <= 2, column waves
+//  ceil(hd/32) <= 4), 4 LDS stages, 4 register slabs, 4 loader wavefronts (2 for items of 1 or 2 compute
+//  wavefronts), one persistent workgroup per compute unit.
+//  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
 //    hold fewer than 8 wavefronts per CU (small steps are latency-bound: more, shorter tiles overlap better);
@@ -158,10 +197,29 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 //  * RC <= 2: the workgroup stages d_dv through a 32 KiB LDS slab, with the XCD-grouped workgroup order.
 //    RC = 4: each wavefront reads d_dv straight from global memory (64 columns of 16 bytes per row: the LDS round
 //    trip measured slower there).
-int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out) {
+// allow_mfma = false forces the vector-ALU engine (row strides too large for the matrix-core engine's 32-bit
+// buffer offsets).
+int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out,
+             bool allow_mfma = true) {
     if (!out) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
-    if (num_cus < 1) num_cus = 256;
+    if (num_cus < 1) num_cus = kDefaultCus;
+    if (allow_mfma && C >= 32 && hd <= 128) {
+        sdm_gx_plan_t p{};
+        p.engine = SDM_GX_ENGINE_MFMA;
+        p.mf_row_waves = C > 64 ? 2 : 1;
+        p.mf_col_waves = static_cast<int32_t>(cdiv(hd, 32) > 2 ? 4 : cdiv(hd, 32));
+        p.mf_stages = 4;
+        p.mf_reg_slabs = 4;
+        p.mf_loader_waves = p.mf_row_waves * p.mf_col_waves <= 2 ? 2 : 4;
+        p.mf_workgroups = num_cus;
+        const int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+        if (st == SDM_GX_OK) {
+            *out = p;
+            return SDM_GX_OK;
+        }
+        if (st != SDM_GX_ERR_LIMIT) return st;
+    }
     int rc = 1;
     int64_t best_waste = cdiv(hd, 64) * 64 - hd;
     for (int cand : {2, 4}) {
@@ -180,6 +238,7 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
     while (waves * 2 <= 8 && waves * 2 <= nrb) waves *= 2;
     while (waves > 1 && nchunks * cdiv(nrb, waves) * ncb < num_cus) waves /= 2;   // at least one workgroup per CU
     sdm_gx_plan_t p{};
+    p.engine = SDM_GX_ENGINE_VALU;
     p.rows_per_wave = ri;
     p.cols_per_lane = rc;
     p.waves_per_wg = waves;
@@ -196,12 +255,41 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
     return SDM_GX_OK;
 }
 
+// The matrix-core engine addresses a chunk of d_u with 32-bit byte offsets.
+bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1) << 31); }
+
 // ---- launching ----------------------------------------------------------------------------------------------------
 // Chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan. Splits very large grids so that one
 // launch stays below 2^31 work-items.
+int launch_mfma(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
+                int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
+    const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages,
+                                                         p.mf_reg_slabs, p.mf_loader_waves);
+    if (!e) return SDM_GX_ERR_PLAN;
+    if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
+    const MfmaGeom g = mfma_geom(p, nchunks, C, hd);
+    if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
+    sdm_gx::MfmaArgs a;
+    a.du = du;
+    a.x = x;
+    a.dv = dv;
+    a.ld_u = ld_u;
+    a.ld_dv = ld_dv;
+    a.n_begin = n_begin;
+    a.n_items = static_cast<int32_t>(g.items);
+    a.per = static_cast<int32_t>(g.per);
+    a.C = static_cast<int32_t>(C);
+    a.hd = static_cast<int32_t>(hd);
+    a.nrg = static_cast<int32_t>(g.nrg);
+    a.ncg = static_cast<int32_t>(g.ncg);
+    const hipError_t err = sdm_gx::launch_mfma_kernel(*e, static_cast<unsigned>(g.grid), stream, a);
+    return err == hipSuccess ? SDM_GX_OK : hip_fail(err);
+}
+
 int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
                   int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
     if (nchunks <= 0) return SDM_GX_OK;
+    if (p.engine == SDM_GX_ENGINE_MFMA) return launch_mfma(p, du, ld_u, x, dv, ld_dv, n_begin, nchunks, C, hd, stream);
     const void* fn = sdm_gx::find_kernel(p.rows_per_wave, p.cols_per_lane, p.waves_per_wg, p.staging);
     if (!fn) return SDM_GX_ERR_PLAN;
     const int64_t nrb = cdiv(C, p.rows_per_wave);
@@ -233,14 +321,18 @@ int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* 
     return SDM_GX_OK;
 }
 
-// Plan (given or planned) for nchunks chunks on a device with `info`.
-int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, const DeviceInfo& info,
-                 sdm_gx_plan_t* out) {
+// Plan (given or planned) for nchunks chunks on a device with `info`; ld_u: the row stride the launch will use.
+int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u,
+                 const DeviceInfo& info, sdm_gx_plan_t* out) {
     if (given) {
         *out = *given;
-        return complete_plan(out, nchunks, C, hd, info.lds_per_wg);
+        if (out->engine == SDM_GX_ENGINE_MFMA && out->mf_workgroups == 0) out->mf_workgroups = info.num_cus;
+        const int st = complete_plan(out, nchunks, C, hd, info.lds_per_wg);
+        if (st) return st;
+        if (out->engine == SDM_GX_ENGINE_MFMA && !mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
+        return SDM_GX_OK;
     }
-    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out);
+    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, mfma_strides_ok(C, ld_u));
 }
 
 int check_device_pointers(const float* du, const float* x, const float* dv, int dev) {
@@ -268,7 +360,7 @@ int sdm_gx_gemm_ex(float* d_u, int64_t ld_u, const float* x, const float* d_dv, 
     if ((st = current_device(&dev, &info))) return st;
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_plan_t p;
-    if ((st = resolve_plan(plan, P, C, hd, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &p))) return st;
     return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, static_cast<hipStream_t>(stream));
 }
 
@@ -298,10 +390,10 @@ int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_d
     sdm_gx_plan_t p;
     if (mode == SDM_GX_STEPS_FUSED) {
         const int64_t nchunks = (ti_end - ti_begin) * P;
-        if ((st = resolve_plan(plan, nchunks, C, hd, info, &p))) return st;
+        if ((st = resolve_plan(plan, nchunks, C, hd, ld_u, info, &p))) return st;
         return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti_begin * P, nchunks, C, hd, s);
     }
-    if ((st = resolve_plan(plan, P, C, hd, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &p))) return st;
     for (int64_t k = 0; k < ti_end - ti_begin; ++k) {
         const int64_t ti = mode == SDM_GX_STEPS_FORWARD ? ti_begin + k : ti_end - 1 - k;
         if ((st = launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, s))) return st;
@@ -321,10 +413,21 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
     if (st) return st;
     if (!info.gfx950) return SDM_GX_ERR_DEVICE;
     if ((st = plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out))) return st;
-    const void* fn = sdm_gx::find_kernel(out->rows_per_wave, out->cols_per_lane, out->waves_per_wg, out->staging);
+    const void* fn;
+    int threads, dyn_lds;
+    if (out->engine == SDM_GX_ENGINE_MFMA) {
+        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(out->mf_row_waves, out->mf_col_waves, out->mf_stages,
+                                                             out->mf_reg_slabs, out->mf_loader_waves);
+        fn = e->fn;
+        threads = 64 * (out->mf_row_waves * out->mf_col_waves + out->mf_loader_waves);
+        dyn_lds = 0;
+    } else {
+        fn = sdm_gx::find_kernel(out->rows_per_wave, out->cols_per_lane, out->waves_per_wg, out->staging);
+        threads = 64 * out->waves_per_wg;
+        dyn_lds = out->lds_bytes;
+    }
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * out->waves_per_wg, out->lds_bytes) ==
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, threads, dyn_lds) == hipSuccess)
         out->wgs_per_cu = blocks;
     else
         (void)hipGetLastError();
@@ -354,8 +457,8 @@ int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* 
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_launch_t l;
     std::memset(&l, 0, sizeof(l));
-    if ((st = resolve_plan(plan, P, C, hd, info, &l.plan_step))) return st;
-    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, info, &l.plan_fused))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &l.plan_step))) return st;
+    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, ld_u, info, &l.plan_fused))) return st;
     l.device = dev;
     l.d_u = d_u;
     l.x = x;
@@ -401,7 +504,14 @@ int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64
 
 int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]) {
     if (!plan || !out) return SDM_GX_ERR_ARG;
-    const void* fn = sdm_gx::find_kernel(plan->rows_per_wave, plan->cols_per_lane, plan->waves_per_wg, plan->staging);
+    const void* fn = nullptr;
+    if (plan->engine == SDM_GX_ENGINE_MFMA) {
+        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(plan->mf_row_waves, plan->mf_col_waves, plan->mf_stages,
+                                                             plan->mf_reg_slabs, plan->mf_loader_waves);
+        if (e) fn = e->fn;
+    } else if (plan->engine == SDM_GX_ENGINE_VALU) {
+        fn = sdm_gx::find_kernel(plan->rows_per_wave, plan->cols_per_lane, plan->waves_per_wg, plan->staging);
+    }
     if (!fn) return SDM_GX_ERR_PLAN;
     hipFuncAttributes a;
     hipError_t e = hipFuncGetAttributes(&a, fn);
@@ -410,7 +520,7 @@ int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]) {
     out[1] = static_cast<int64_t>(a.localSizeBytes);
     out[2] = static_cast<int64_t>(a.sharedSizeBytes);
     out[3] = a.maxThreadsPerBlock;
-    out[4] = plan->lds_bytes;
+    out[4] = plan->engine == SDM_GX_ENGINE_MFMA ? 0 : plan->lds_bytes;
     return SDM_GX_OK;
 }
 
@@ -423,7 +533,7 @@ const char* sdm_gx_strerror(int code) {
         case SDM_GX_ERR_ALIGN: return "pointer not 4-byte aligned";
         case SDM_GX_ERR_OVERLAP: return "d_u overlaps x or d_dv (the in-place update needs disjoint operands)";
         case SDM_GX_ERR_STRIDE: return "row stride out of range (need hd <= ld < 2^31)";
-        case SDM_GX_ERR_LIMIT: return "launch exceeds a device limit";
+        case SDM_GX_ERR_LIMIT: return "launch exceeds a device or engine limit";
         case SDM_GX_ERR_HIP: return "HIP runtime error (see sdm_gx_last_hip_error)";
         case SDM_GX_ERR_PLAN: return "invalid plan or prepared launch";
         case SDM_GX_ERR_DEVICE: return "no gfx950 device, or a pointer / prepared launch is not on the current device";

@@ -1,0 +1,36 @@
+// Internal interface between the matrix-core kernels and the host entry points of libsdm_gx_gemm (not the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm_gx {
+
+// Work items are (chunk, row group, column group) tiles; workgroup b takes items b*per .. b*per + per - 1 of chunks
+// n_begin .. n_begin + n_items / (nrg * ncg) - 1.
+struct MfmaArgs {
+    float* du;
+    const float* x;
+    const float* dv;
+    int64_t ld_u;
+    int64_t ld_dv;
+    int64_t n_begin;
+    int32_t n_items;    // work items of the launch (< 2^31)
+    int32_t per;        // items per workgroup
+    int32_t C;
+    int32_t hd;
+    int32_t nrg;        // row groups per chunk: ceil(ceil(C / 64) / row_waves)
+    int32_t ncg;        // column groups per chunk: ceil(hd / (32 * col_waves))
+};
+
+struct MfmaEntry {
+    int row_waves, col_waves, stages, reg_slabs, loader_waves;
+    const void* fn;
+    int lds_bytes;      // static LDS of the instance
+};
+
+// The kernel instance for the given shape parameters, or nullptr.
+const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves);
+hipError_t launch_mfma_kernel(const MfmaEntry& e, unsigned grid, hipStream_t stream, const MfmaArgs& a);
+
+}  // namespace sdm_gx

@@ -10,9 +10,11 @@
  *       d_u[n, i, c] = d_u[n, i, c] + acc        (one separately rounded IEEE binary32 add, in place)
  *
  * Every fused multiply-add and the final add round to nearest even and keep subnormals. Each output element is
- * computed by one GPU lane running exactly that chain, so results are bit-identical for every launch plan, step
- * order and run, and equal to the CPU definition wherever the result is not NaN (NaN results are NaN on both
- * sides; their payload is not specified).
+ * computed by exactly that chain, either by one GPU lane on the vector ALUs (engine SDM_GX_ENGINE_VALU) or on the
+ * FP32 matrix cores as one K=1 MFMA per chain step (engine SDM_GX_ENGINE_MFMA: d = c + a*b, a single rounding, no
+ * reduction inside the instruction). Results are bit-identical for every engine, launch plan, step order and run,
+ * and equal to the CPU definition wherever the result is not NaN (NaN results are NaN on both sides; their payload
+ * is not specified).
  *
  * Memory layout (FP32, row-major; element offsets):
  *   x     [N][C][C]               x[n, j, i]    at (n*C + j)*C + i        (contiguous; used transposed)
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SDM_GX_ABI_VERSION 1
+#define SDM_GX_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define SDM_GX_API __attribute__((visibility("default")))
@@ -65,7 +67,8 @@ typedef enum sdm_gx_status {
     SDM_GX_ERR_ALIGN = -4,     /* a pointer is not 4-byte aligned */
     SDM_GX_ERR_OVERLAP = -5,   /* d_u overlaps x or d_dv */
     SDM_GX_ERR_STRIDE = -6,    /* ld_u or ld_dv < hd, or >= 2^31 */
-    SDM_GX_ERR_LIMIT = -7,     /* the launch exceeds a device limit (LDS per workgroup) */
+    SDM_GX_ERR_LIMIT = -7,     /* the launch exceeds a device or engine limit (LDS per workgroup; for the MFMA
+                                  engine C * ld_u * 4 must stay below 2^31 bytes) */
     SDM_GX_ERR_HIP = -8,       /* a HIP runtime call failed: see sdm_gx_last_hip_error() */
     SDM_GX_ERR_PLAN = -9,      /* a plan / prepared launch is malformed or does not fit this shape */
     SDM_GX_ERR_DEVICE = -10,   /* no usable gfx950 device, pointers not on the current device, or a prepared
@@ -73,7 +76,14 @@ typedef enum sdm_gx_status {
     SDM_GX_ERR_ARG = -11       /* any other invalid argument (unknown mode, NULL output struct, ...) */
 } sdm_gx_status;
 
-/* A launch plan: how output tiles map onto wavefronts and workgroups. Results never depend on it.
+/* Engines (sdm_gx_plan_t.engine). */
+#define SDM_GX_ENGINE_VALU 0   /* one lane per output element, v_fma_f32 chains on the vector ALUs */
+#define SDM_GX_ENGINE_MFMA 1   /* the same chains on the FP32 matrix cores, one K=1 MFMA per chain step */
+
+/* A launch plan: which engine runs the update and how output tiles map onto wavefronts and workgroups. Results
+ * never depend on it.
+ *   engine         SDM_GX_ENGINE_VALU or SDM_GX_ENGINE_MFMA
+ * SDM_GX_ENGINE_VALU (the other engine ignores these fields):
  *   rows_per_wave  RI: output rows one wavefront owns (1, 2, 4, 8 or 16; RI <= C)
  *   cols_per_lane  RC: adjacent output columns one lane owns (1, 2 or 4); a wavefront covers 64*RC columns
  *   waves_per_wg   wavefronts per workgroup (1, 2, 4, 8, or 16 for some tiles); they take consecutive row blocks of
@@ -82,18 +92,35 @@ typedef enum sdm_gx_status {
  *                  1: the workgroup stages its d_dv column block in LDS once and every wavefront reads it there
  *   xcd_remap      1: workgroup ids are permuted so that the workgroups of one chunk run on one XCD (one L2)
  *   slab_rows      staging 1: d_dv rows per LDS slab (0: the planner's choice; clamped to C)
- *   lds_bytes      (output of the planner) dynamic LDS bytes per workgroup
- *   wgs_per_cu     (output of the planner) workgroups per CU that can be resident (0 if not known)
- *   grid           (output of the planner) workgroups for the chunk count it was planned for */
+ * SDM_GX_ENGINE_MFMA (persistent workgroups walking (chunk, row group, column group) work items; the other engine
+ * ignores these fields):
+ *   mf_row_waves     compute wavefronts along the rows of a work item, 64 rows each (1 or 2)
+ *   mf_col_waves     compute wavefronts along its columns, 32 columns each (1, 2, 4, or 8 with mf_row_waves 1)
+ *   mf_stages        LDS ring stages of 16 chain rows of x and d_dv (4)
+ *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4)
+ *   mf_loader_waves  loader wavefronts per workgroup (2 or 4; 4 with 4 register slabs for 64x256 and 128x128 items)
+ *   mf_workgroups    workgroups to launch (0: one per compute unit); each takes a contiguous range of work items
+ * Outputs of the planner / sdm_gx_plan_complete:
+ *   lds_bytes      LDS bytes per workgroup (dynamic for the VALU engine, static for the MFMA engine)
+ *   wgs_per_cu     workgroups per CU that can be resident (0 if not known)
+ *   grid           workgroups for the chunk count it was planned for */
 typedef struct sdm_gx_plan {
+    int32_t engine;
     int32_t rows_per_wave;
     int32_t cols_per_lane;
     int32_t waves_per_wg;
     int32_t staging;
     int32_t xcd_remap;
     int32_t slab_rows;
+    int32_t mf_row_waves;
+    int32_t mf_col_waves;
+    int32_t mf_stages;
+    int32_t mf_reg_slabs;
+    int32_t mf_loader_waves;
+    int32_t mf_workgroups;
     int32_t lds_bytes;
     int32_t wgs_per_cu;
+    int32_t reserved;
     int64_t grid;
 } sdm_gx_plan_t;
 
@@ -164,8 +191,8 @@ SDM_GX_API int sdm_gx_launch(const sdm_gx_launch_t* prepared, int64_t ti, void* 
 /* Issue steps ti_begin .. ti_end - 1 of a prepared launch as ONE launch (every ti <= ti_max). */
 SDM_GX_API int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64_t ti_end, void* stream);
 
-/* Resource usage of the kernel instance a plan selects (the page's gx_gemm_attrs): out[0] architectural VGPRs per
- * lane, out[1] private (scratch) bytes per lane, out[2] static LDS bytes, out[3] max threads per workgroup,
+/* Resource usage of the kernel instance a plan selects (the page's gx_gemm_attrs): out[0] VGPRs per lane,
+ * out[1] private (scratch) bytes per lane, out[2] static LDS bytes, out[3] max threads per workgroup,
  * out[4] the plan's dynamic LDS bytes. Needs a device. */
 SDM_GX_API int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]);
 

@@ -41,7 +41,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_abi_version():
-    assert g.sdm_gx_abi_version() == 1
+    assert g.sdm_gx_abi_version() == 2
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -51,9 +51,11 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "sdm_gx_gemm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
          sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
-         offsetof(sdm_gx_launch_t, plan_fused));
+         offsetof(sdm_gx_launch_t, plan_fused), offsetof(sdm_gx_plan_t, slab_rows),
+         offsetof(sdm_gx_plan_t, mf_row_waves), offsetof(sdm_gx_plan_t, mf_workgroups),
+         offsetof(sdm_gx_plan_t, lds_bytes));
   return 0;
 }
 """)
@@ -62,7 +64,9 @@ int main(void) {
     vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert vals == [ctypes.sizeof(g.sdm_gx_plan_t), g.sdm_gx_plan_t.grid.offset, ctypes.sizeof(g.sdm_gx_launch_t),
                     g.sdm_gx_launch_t.ti_max.offset, g.sdm_gx_launch_t.plan_step.offset,
-                    g.sdm_gx_launch_t.plan_fused.offset]
+                    g.sdm_gx_launch_t.plan_fused.offset, g.sdm_gx_plan_t.slab_rows.offset,
+                    g.sdm_gx_plan_t.mf_row_waves.offset, g.sdm_gx_plan_t.mf_workgroups.offset,
+                    g.sdm_gx_plan_t.lds_bytes.offset]
 
 
 def test_strerror_covers_every_code():
@@ -120,18 +124,40 @@ def test_check_codes(kw, code):
     assert chk(**kw) == code
 
 
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def mfma_grid(items, workgroups=256):
+    if items == 0:
+        return 0
+    per = cdiv(items, min(items, workgroups))
+    return cdiv(items, per)
+
+
 def test_plan_for_emits_supported_plans():
-    shapes = [(C, hd) for C in (1, 2, 3, 4, 5, 16, 17, 31, 64, 100, 128, 200, 256)
+    shapes = [(C, hd) for C in (1, 2, 3, 4, 5, 16, 17, 31, 32, 64, 100, 128, 200, 256)
               for hd in (1, 3, 4, 63, 64, 65, 100, 128, 129, 200, 256, 257, 1000, 4100)]
     for nchunks in (0, 1, 7, 128, 4096):
         for C, hd in shapes:
             p = g.sdm_gx_plan_for(nchunks, C, hd)
+            # engine rule: matrix cores for 32 <= C and hd <= 128
+            assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and hd <= 128 else g.SDM_GX_ENGINE_VALU)
+            if p.engine == g.SDM_GX_ENGINE_MFMA:
+                assert p.mf_row_waves == (2 if C > 64 else 1)
+                assert p.mf_col_waves == (4 if cdiv(hd, 32) > 2 else cdiv(hd, 32))
+                assert (p.mf_stages, p.mf_reg_slabs) == (4, 4) and p.mf_workgroups == 256
+                assert p.mf_loader_waves == (2 if p.mf_row_waves * p.mf_col_waves <= 2 else 4)
+                items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 32 * p.mf_col_waves)
+                assert p.grid == mfma_grid(items)
+                assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 8 * p.mf_col_waves)
+                continue
             assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
             assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
             assert p.waves_per_wg in (1, 2, 4, 8)
-            nrb = -(-C // p.rows_per_wave)
-            nrg = -(-nrb // p.waves_per_wg)
-            ncb = -(-hd // (64 * p.cols_per_lane))
+            nrb = cdiv(C, p.rows_per_wave)
+            nrg = cdiv(nrb, p.waves_per_wg)
+            ncb = cdiv(hd, 64 * p.cols_per_lane)
             assert p.grid == nchunks * nrg * ncb
             assert p.lds_bytes <= 64 * 1024
 
@@ -139,7 +165,8 @@ def test_plan_for_emits_supported_plans():
 @pytest.mark.parametrize("bad", [
     dict(rows_per_wave=3), dict(rows_per_wave=64), dict(cols_per_lane=3), dict(waves_per_wg=3),
     dict(waves_per_wg=32), dict(staging=2), dict(xcd_remap=2), dict(slab_rows=-1),
-    dict(rows_per_wave=32), dict(rows_per_wave=16, cols_per_lane=4, waves_per_wg=16),
+    dict(rows_per_wave=32), dict(rows_per_wave=16, cols_per_lane=4, waves_per_wg=16), dict(engine=2),
+    dict(engine=-1),
 ])
 def test_plan_complete_rejects(bad):
     p = g.make_plan(8, 1, 4)
@@ -148,6 +175,33 @@ def test_plan_complete_rejects(bad):
     with pytest.raises(ValueError):
         g.sdm_gx_plan_complete(p, 4, 64, 64)
 
+
+@pytest.mark.parametrize("bad", [
+    dict(mf_row_waves=3), dict(mf_row_waves=0), dict(mf_col_waves=3), dict(mf_col_waves=16),
+    dict(mf_row_waves=2, mf_col_waves=8), dict(mf_stages=3), dict(mf_stages=2), dict(mf_reg_slabs=3),
+    dict(mf_loader_waves=1), dict(mf_loader_waves=8), dict(mf_workgroups=-1),
+    dict(mf_col_waves=8, mf_reg_slabs=4, mf_loader_waves=2),        # left out of the table: it spills
+    dict(mf_row_waves=2, mf_col_waves=4, mf_reg_slabs=4, mf_loader_waves=2),
+])
+def test_mfma_plan_complete_rejects(bad):
+    p = g.make_mfma_plan(1, 4)
+    for k, v in bad.items():
+        setattr(p, k, v)
+    with pytest.raises(ValueError):
+        g.sdm_gx_plan_complete(p, 4, 64, 64)
+
+
+MFMA_INSTANCES = [(rw, cw, rs, lw) for rw in (1, 2) for cw in (1, 2, 4, 8) for rs in (2, 4) for lw in (2, 4)
+                  if not (rw == 2 and cw == 8) and (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))]
+
+
+@pytest.mark.parametrize("rw,cw,rs,lw", MFMA_INSTANCES)
+def test_mfma_plan_complete_geometry(rw, cw, rs, lw):
+    for nchunks, C, hd, wgs in ((512, 128, 128, 0), (7, 200, 33, 3), (1, 1, 1, 0), (1000, 64, 256, 100), (0, 64, 64, 0)):
+        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, 4, rs, lw, wgs), nchunks, C, hd)
+        items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, 32 * cw)
+        assert p.grid == mfma_grid(items, wgs or 256)
+        assert p.lds_bytes == 16 * 4 * 16 * (16 * rw + 8 * cw)
 
 def test_plan_complete_rows_beyond_c():
     with pytest.raises(ValueError):

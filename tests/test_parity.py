@@ -84,7 +84,9 @@ def test_workload_bench_launch(key):
 
 # ---- every plan gives the same bits --------------------------------------------------------------------------------
 def all_plans(C, hd=64):
-    """Every plan the library has a kernel instance for (plans without one are rejected by the library)."""
+    """Every plan the library has a kernel instance for (plans without one are rejected by the library): every
+    vector-ALU tile and staging, and every matrix-core instance with one workgroup per CU and with two workgroups in
+    all (so that each walks several work items)."""
     for ri in (1, 2, 4, 8, 16, 32):
         if ri > C:
             continue
@@ -100,6 +102,17 @@ def all_plans(C, hd=64):
                             except ValueError:
                                 continue
                             yield plan
+    for rw in (1, 2):
+        for cw in (1, 2, 4, 8):
+            for rs in (2, 4):
+                for lw in (2, 4):
+                    for wgs in (0, 2):
+                        plan = g.make_mfma_plan(rw, cw, 4, rs, lw, wgs)
+                        try:
+                            g.sdm_gx_plan_complete(plan, 1, C, hd)
+                        except ValueError:
+                            continue
+                        yield plan
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8)])
@@ -115,7 +128,44 @@ def test_every_plan_is_bit_identical(C, hd, ld, res):
         got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FORWARD, plan)
         assert_matches(got, want, du, hd, f"plan {plan}")
         n += 1
-    assert n > 50
+    assert n > 100
+
+
+@pytest.mark.parametrize("C", [1, 5, 16, 17, 20, 33, 64, 65, 128, 130])
+def test_signed_zero_through_padded_steps(C):
+    """Products that round to -0 keep the accumulator at -0, and -0 + -0 stays -0 in d_u. The matrix-core engine
+    pads the last slab's chain rows (and items' missing rows) with a -0 product, which must leave such an
+    accumulator untouched; a +0 padding product would turn the result into +0."""
+    N, P, hd, ld = 4, 2, 40, 44
+    x = np.full((N, C, C), -1e-30, np.float32)
+    dv = np.full((N, C, ld), 1e-30, np.float32)
+    du = np.full((N, C, ld), -0.0, np.float32)
+    du[:, :, hd:] = np.float32(3.5)                            # padding columns: must stay untouched
+    want = expected(x, dv, du, hd, 0, N)
+    assert (np.signbit(want[:, :, :hd])).all() and (want[:, :, :hd] == 0).all()
+    case = DeviceCase(x, dv, du, hd, res_u=4, res_v=8, res_x=12)
+    plans = [None, g.make_mfma_plan(1, 2, 4, 4, 2), g.make_mfma_plan(2, 1, 4, 2, 4, 1), g.make_plan(1, 1, 2, 1, 1)]
+    for plan in plans:
+        case.reset()
+        say(f"signed zero C={C} plan {plan}")
+        got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, plan)
+        assert_matches(got, want, du, hd, f"signed zero C={C} plan {plan}")
+
+
+def test_mfma_engine_many_items_per_workgroup():
+    """Persistent matrix-core workgroups walking long ranges of work items (chunks x row groups x column groups),
+    ragged in rows and columns, per step and fused."""
+    N, P, C, hd, ld = 30, 5, 150, 70, 73
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=77)
+    case = DeviceCase(x, dv, du, hd, res_u=4, res_v=0, res_x=8)
+    want = expected(x, dv, du, hd, 0, N)
+    for plan in (g.make_mfma_plan(2, 2, 4, 4, 4, 3), g.make_mfma_plan(1, 1, 4, 2, 2, 7),
+                 g.make_mfma_plan(1, 8, 4, 2, 2, 1), g.make_mfma_plan(2, 4, 4, 4, 4, 0)):
+        for mode in (g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_FUSED):
+            case.reset()
+            say(f"mfma items plan {plan} mode {mode}")
+            got = run_steps(case, P, 0, N // P, mode, plan)
+            assert_matches(got, want, du, hd, f"mfma plan {plan} mode {mode}")
 
 
 # ---- driver modes ----------------------------------------------------------------------------------------------------
@@ -227,17 +277,23 @@ def test_errors_launch_nothing():
 
 
 def test_no_kernel_instance_spills():
-    """Every kernel instance runs without private (scratch) memory."""
+    """Every kernel instance runs without private (scratch) memory, and its workgroup fits one CU's registers."""
     seen = set()
     for plan in all_plans(256, 4096):
-        key = (plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
+        if plan.engine == g.SDM_GX_ENGINE_MFMA:
+            key = ("mfma", plan.mf_row_waves, plan.mf_col_waves, plan.mf_stages, plan.mf_reg_slabs,
+                   plan.mf_loader_waves)
+            waves = plan.mf_row_waves * plan.mf_col_waves + plan.mf_loader_waves
+        else:
+            key = ("valu", plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
+            waves = plan.waves_per_wg
         if key in seen:
             continue
         seen.add(key)
         attrs = g.sdm_gx_kernel_attrs(plan)
         assert attrs["scratch_bytes"] == 0, (key, attrs)
-        assert attrs["vgprs"] * plan.waves_per_wg <= 512 * 4 or plan.waves_per_wg < 16, (key, attrs)
-    assert len(seen) > 100
+        assert attrs["vgprs"] * -(-waves // 4) <= 512, (key, attrs)
+    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 26
 
 
 def test_kernel_attrs_report_no_scratch():

@@ -152,6 +152,28 @@ def test_signed_zero_through_padded_steps(C):
         assert_matches(got, want, du, hd, f"signed zero C={C} plan {plan}")
 
 
+def test_mfma_engine_single_rounding():
+    """Two-step chains on near-cancelling inputs: acc = fma(x1, d1, fl(x0*d0)), where a fused and an unfused second
+    step round differently for a large share of the outputs. The matrix-core engine (one K=1 MFMA per step) must
+    give the fused result: the oracle's fmaf chain, bit for bit."""
+    rng = np.random.default_rng(2026)
+    N, P, C, hd = 512, 8, 2, 64
+    x = rng.standard_normal((N, C, C)).astype(np.float32)
+    dv = np.empty((N, C, hd), np.float32)
+    dv[:, 0, :] = rng.standard_normal((N, hd)).astype(np.float32)
+    # row 1 nearly cancels row 0's product for output row 0: x[n,1,0]*dv[n,1,c] ~ -x[n,0,0]*dv[n,0,c]
+    dv[:, 1, :] = (-(x[:, 0, 0:1].astype(np.float64) * dv[:, 0, :]) / x[:, 1, 0:1]).astype(np.float32)
+    du = np.zeros((N, C, hd), np.float32)
+    want = expected(x, dv, du, hd, 0, N)
+    p0 = (x[:, 0, 0:1] * dv[:, 0, :]).astype(np.float32)                 # fl(x0*d0): float32 products
+    unfused = (p0 + (x[:, 1, 0:1] * dv[:, 1, :]).astype(np.float32)).astype(np.float32)
+    differ = unfused.view(np.uint32) != want[:, 0, :].view(np.uint32)
+    assert differ.mean() > 0.2, differ.mean()                             # the test has teeth
+    case = DeviceCase(x, dv, du, hd)
+    got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, g.make_mfma_plan(1, 2, 4, 4, 2))
+    assert_matches(got, want, du, hd, "mfma single rounding")
+
+
 def test_mfma_engine_many_items_per_workgroup():
     """Persistent matrix-core workgroups walking long ranges of work items (chunks x row groups x column groups),
     ragged in rows and columns, per step and fused."""

@@ -65,7 +65,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5))
-    ap.add_argument("--driver", default="fused", choices=("fused", "per-step"))
+    ap.add_argument("--driver", default="fused", choices=("fused", "per-step", "graph"),
+                    help="fused: one launch for all T steps; per-step: T launches; graph: one replay of a HIP graph "
+                         "holding the T per-step launches")
     ap.add_argument("--cold", action="store_true", help="flush the caches before every timed launch (adds a field)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -114,9 +116,13 @@ def main():
     step = g.make_step(du3, x3, dv3, P, plan)
     stream = torch.cuda.current_stream()
 
+    graph = step.graph(0, T, g.SDM_GX_STEPS_FORWARD) if args.driver == "graph" else None
+
     def one_pass():
         if args.driver == "fused":
             step.fused(0, T, stream)
+        elif args.driver == "graph":
+            graph.launch(stream)
         else:
             for ti in range(T):
                 step(ti, stream)
@@ -151,12 +157,12 @@ def main():
 
     # Per-launch spread: an event pair around each launch (adds the events' own overhead, ~2 us, to each figure).
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(args.steps, 200) * launches_per_pass)]
+          for _ in range(min(args.steps, 200) * (1 if args.driver == "graph" else launches_per_pass))]
     k = 0
     for _ in range(min(args.steps, 200)):
-        if args.driver == "fused":
+        if args.driver in ("fused", "graph"):
             ev[k][0].record(stream)
-            step.fused(0, T, stream)
+            one_pass()
             ev[k][1].record(stream)
             k += 1
         else:

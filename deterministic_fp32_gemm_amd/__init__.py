@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     SDM_GX_STEPS_FORWARD,
     SDM_GX_STEPS_FUSED,
     SDM_GX_STEPS_REVERSE,
+    Graph,
     load,
     make_mfma_plan,
     make_plan,
@@ -33,6 +34,10 @@ from ._binding import (  # noqa: F401
     sdm_gx_gemm,
     sdm_gx_gemm_ex,
     sdm_gx_gemm_steps,
+    sdm_gx_graph_create,
+    sdm_gx_graph_destroy,
+    sdm_gx_graph_launch,
+    sdm_gx_graph_nodes,
     sdm_gx_kernel_attrs,
     sdm_gx_last_hip_error,
     sdm_gx_launch,

@@ -65,7 +65,8 @@ class sdm_gx_launch_t(ctypes.Structure):
 
 
 EXPORTS = ("sdm_gx_gemm", "sdm_gx_gemm_ex", "sdm_gx_gemm_steps", "sdm_gx_check", "sdm_gx_plan", "sdm_gx_plan_for",
-           "sdm_gx_plan_complete", "sdm_gx_prepare", "sdm_gx_launch", "sdm_gx_launch_fused", "sdm_gx_kernel_attrs",
+           "sdm_gx_plan_complete", "sdm_gx_prepare", "sdm_gx_launch", "sdm_gx_launch_fused", "sdm_gx_graph_create",
+           "sdm_gx_graph_launch", "sdm_gx_graph_nodes", "sdm_gx_graph_destroy", "sdm_gx_kernel_attrs",
            "sdm_gx_strerror", "sdm_gx_last_hip_error", "sdm_gx_abi_version")
 
 _lib = None
@@ -104,11 +105,15 @@ def load() -> ctypes.CDLL:
             "sdm_gx_strerror": [ctypes.c_int],
             "sdm_gx_last_hip_error": [],
             "sdm_gx_abi_version": [],
+            "sdm_gx_graph_create": [ctypes.POINTER(_vp), _LP, _i64, _i64, _i32],
+            "sdm_gx_graph_launch": [_vp, _vp],
+            "sdm_gx_graph_nodes": [_vp],
+            "sdm_gx_graph_destroy": [_vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "sdm_gx_strerror" else ctypes.c_int
+            fn.restype = {"sdm_gx_strerror": ctypes.c_char_p, "sdm_gx_graph_nodes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = lib
         return lib
 
@@ -238,6 +243,53 @@ def sdm_gx_launch(prepared: sdm_gx_launch_t, ti, stream=None) -> None:
 def sdm_gx_launch_fused(prepared: sdm_gx_launch_t, ti_begin, ti_end, stream=None) -> None:
     _raise(load().sdm_gx_launch_fused(ctypes.byref(prepared), int(ti_begin), int(ti_end), _stream(stream)),
            "sdm_gx_launch_fused")
+
+
+class Graph:
+    """A HIP graph of a prepared step range (sdm_gx_graph_create). launch(stream) replays it; close() (or garbage
+    collection) releases it. Keeps the prepared launch it was built from alive."""
+
+    def __init__(self, prepared: sdm_gx_launch_t, ti_begin, ti_end, mode=SDM_GX_STEPS_FUSED):
+        self._h = ctypes.c_void_p()
+        self._prepared = prepared
+        _raise(load().sdm_gx_graph_create(ctypes.byref(self._h), ctypes.byref(prepared), int(ti_begin), int(ti_end),
+                                          int(mode)), "sdm_gx_graph_create")
+
+    @property
+    def nodes(self) -> int:
+        return int(load().sdm_gx_graph_nodes(self._h)) if self._h else -1
+
+    def launch(self, stream=None) -> None:
+        if not self._h:
+            raise ValueError("graph already closed")
+        _raise(load().sdm_gx_graph_launch(self._h, _stream(stream)), "sdm_gx_graph_launch")
+
+    def close(self) -> None:
+        if self._h:
+            h, self._h = self._h, ctypes.c_void_p()
+            _raise(load().sdm_gx_graph_destroy(h), "sdm_gx_graph_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sdm_gx_graph_create(prepared: sdm_gx_launch_t, ti_begin, ti_end, mode=SDM_GX_STEPS_FUSED) -> Graph:
+    return Graph(prepared, ti_begin, ti_end, mode)
+
+
+def sdm_gx_graph_launch(graph: Graph, stream=None) -> None:
+    graph.launch(stream)
+
+
+def sdm_gx_graph_nodes(graph: Graph) -> int:
+    return graph.nodes
+
+
+def sdm_gx_graph_destroy(graph: Graph) -> None:
+    graph.close()
 
 
 def sdm_gx_kernel_attrs(plan: sdm_gx_plan_t) -> dict:

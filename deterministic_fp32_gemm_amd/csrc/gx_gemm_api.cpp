@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "../../include/sdm_gx_gemm.h"
@@ -261,35 +262,52 @@ bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1
 // ---- launching ----------------------------------------------------------------------------------------------------
 // Chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan. Splits very large grids so that one
 // launch stays below 2^31 work-items.
-int launch_mfma(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
-                int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
-    const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages,
-                                                         p.mf_reg_slabs, p.mf_loader_waves);
-    if (!e) return SDM_GX_ERR_PLAN;
-    if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
-    const MfmaGeom g = mfma_geom(p, nchunks, C, hd);
-    if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
-    sdm_gx::MfmaArgs a;
-    a.du = du;
-    a.x = x;
-    a.dv = dv;
-    a.ld_u = ld_u;
-    a.ld_dv = ld_dv;
-    a.n_begin = n_begin;
-    a.n_items = static_cast<int32_t>(g.items);
-    a.per = static_cast<int32_t>(g.per);
-    a.C = static_cast<int32_t>(C);
-    a.hd = static_cast<int32_t>(hd);
-    a.nrg = static_cast<int32_t>(g.nrg);
-    a.ncg = static_cast<int32_t>(g.ncg);
-    const hipError_t err = sdm_gx::launch_mfma_kernel(*e, static_cast<unsigned>(g.grid), stream, a);
-    return err == hipSuccess ? SDM_GX_OK : hip_fail(err);
-}
+// One kernel launch: function, shape and the argument block it takes by value.
+struct LaunchRec {
+    const void* fn = nullptr;
+    unsigned grid = 0, block = 0, lds = 0;
+    bool mfma = false;
+    sdm_gx::KernelArgs va{};
+    sdm_gx::MfmaArgs ma{};
+    void* args() const { return mfma ? const_cast<sdm_gx::MfmaArgs*>(&ma) : static_cast<void*>(const_cast<sdm_gx::KernelArgs*>(&va)); }
+};
 
-int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
-                  int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
+// The kernel launches that update chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan, in
+// order, each handed to sink(const LaunchRec&) -> hipError_t. The vector-ALU engine splits very large grids so that
+// one launch stays below 2^31 work-items; the matrix-core engine is one launch.
+template <class Sink>
+int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
+                    int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, Sink&& sink) {
     if (nchunks <= 0) return SDM_GX_OK;
-    if (p.engine == SDM_GX_ENGINE_MFMA) return launch_mfma(p, du, ld_u, x, dv, ld_dv, n_begin, nchunks, C, hd, stream);
+    LaunchRec r;
+    if (p.engine == SDM_GX_ENGINE_MFMA) {
+        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages,
+                                                             p.mf_reg_slabs, p.mf_loader_waves);
+        if (!e) return SDM_GX_ERR_PLAN;
+        if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
+        const MfmaGeom g = mfma_geom(p, nchunks, C, hd);
+        if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
+        r.mfma = true;
+        r.fn = e->fn;
+        r.grid = static_cast<unsigned>(g.grid);
+        r.block = 64u * static_cast<unsigned>(e->row_waves * e->col_waves + e->loader_waves);
+        r.lds = 0;
+        sdm_gx::MfmaArgs& a = r.ma;
+        a.du = du;
+        a.x = x;
+        a.dv = dv;
+        a.ld_u = ld_u;
+        a.ld_dv = ld_dv;
+        a.n_begin = n_begin;
+        a.n_items = static_cast<int32_t>(g.items);
+        a.per = static_cast<int32_t>(g.per);
+        a.C = static_cast<int32_t>(C);
+        a.hd = static_cast<int32_t>(hd);
+        a.nrg = static_cast<int32_t>(g.nrg);
+        a.ncg = static_cast<int32_t>(g.ncg);
+        const hipError_t err = sink(static_cast<const LaunchRec&>(r));
+        return err == hipSuccess ? SDM_GX_OK : hip_fail(err);
+    }
     const void* fn = sdm_gx::find_kernel(p.rows_per_wave, p.cols_per_lane, p.waves_per_wg, p.staging);
     if (!fn) return SDM_GX_ERR_PLAN;
     const int64_t nrb = cdiv(C, p.rows_per_wave);
@@ -299,7 +317,10 @@ int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* 
     const int64_t max_blocks = (int64_t(1) << 31) / (64 * p.waves_per_wg);
     int64_t step = max_blocks / per_chunk;
     if (step < 1) return SDM_GX_ERR_LIMIT;
-    sdm_gx::KernelArgs a;
+    r.fn = fn;
+    r.block = 64u * static_cast<unsigned>(p.waves_per_wg);
+    r.lds = static_cast<unsigned>(p.lds_bytes);
+    sdm_gx::KernelArgs& a = r.va;
     a.du = du;
     a.x = x;
     a.dv = dv;
@@ -314,11 +335,19 @@ int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* 
     for (int64_t s = 0; s < nchunks; s += step) {
         const int64_t cnt = nchunks - s < step ? nchunks - s : step;
         a.n_begin = n_begin + s;
-        const hipError_t e = sdm_gx::launch_kernel(fn, p.waves_per_wg, static_cast<unsigned>(cnt * per_chunk),
-                                                   static_cast<unsigned>(p.lds_bytes), stream, a);
+        r.grid = static_cast<unsigned>(cnt * per_chunk);
+        const hipError_t e = sink(static_cast<const LaunchRec&>(r));
         if (e != hipSuccess) return hip_fail(e);
     }
     return SDM_GX_OK;
+}
+
+int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* x, const float* dv, int64_t ld_dv,
+                  int64_t n_begin, int64_t nchunks, int64_t C, int64_t hd, hipStream_t stream) {
+    return for_each_launch(p, du, ld_u, x, dv, ld_dv, n_begin, nchunks, C, hd, [stream](const LaunchRec& r) {
+        void* args[] = {r.args()};
+        return hipLaunchKernel(r.fn, dim3(r.grid), dim3(r.block), args, r.lds, stream);
+    });
 }
 
 // Plan (given or planned) for nchunks chunks on a device with `info`; ld_u: the row stride the launch will use.
@@ -500,6 +529,108 @@ int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64
     if (ti_begin < 0 || ti_end < ti_begin || ti_end > l.ti_max + 1) return SDM_GX_ERR_STEP;
     return launch_chunks(l.plan_fused, l.d_u, l.ld_u, l.x, l.d_dv, l.ld_dv, ti_begin * l.P, (ti_end - ti_begin) * l.P,
                          l.C, l.hd, static_cast<hipStream_t>(stream));
+}
+
+// ---- HIP graphs of a prepared step range --------------------------------------------------------------------------
+struct sdm_gx_graph {
+    uint64_t magic;
+    int32_t device;
+    int64_t nodes;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+constexpr uint64_t kGraphMagic = 0x4850415247584753ull;   // graph tag
+
+int sdm_gx_graph_create(sdm_gx_graph_t** out, const sdm_gx_launch_t* prepared, int64_t ti_begin, int64_t ti_end,
+                        int32_t mode) {
+    if (!out) return SDM_GX_ERR_ARG;
+    *out = nullptr;
+    if (mode != SDM_GX_STEPS_FORWARD && mode != SDM_GX_STEPS_REVERSE && mode != SDM_GX_STEPS_FUSED)
+        return SDM_GX_ERR_ARG;
+    int st = prepared_ok(prepared);
+    if (st) return st;
+    const sdm_gx_launch_t& l = *prepared;
+    if (ti_begin < 0 || ti_end < ti_begin || ti_end > l.ti_max + 1) return SDM_GX_ERR_STEP;
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipGraphCreate(&graph, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    hipGraphNode_t prev = nullptr;
+    int64_t nodes = 0;
+    auto add = [&](const LaunchRec& r) {               // kernel nodes in issue order, each after the previous one
+        hipKernelNodeParams np{};
+        void* args[] = {r.args()};
+        np.func = const_cast<void*>(r.fn);
+        np.gridDim = dim3(r.grid);
+        np.blockDim = dim3(r.block);
+        np.sharedMemBytes = r.lds;
+        np.kernelParams = args;
+        np.extra = nullptr;
+        hipGraphNode_t node = nullptr;
+        const hipError_t err = hipGraphAddKernelNode(&node, graph, prev ? &prev : nullptr, prev ? 1 : 0, &np);
+        if (err == hipSuccess) {
+            prev = node;
+            ++nodes;
+        }
+        return err;
+    };
+    if (mode == SDM_GX_STEPS_FUSED) {
+        st = for_each_launch(l.plan_fused, l.d_u, l.ld_u, l.x, l.d_dv, l.ld_dv, ti_begin * l.P,
+                             (ti_end - ti_begin) * l.P, l.C, l.hd, add);
+    } else {
+        for (int64_t k = 0; k < ti_end - ti_begin && !st; ++k) {
+            const int64_t ti = mode == SDM_GX_STEPS_FORWARD ? ti_begin + k : ti_end - 1 - k;
+            st = for_each_launch(l.plan_step, l.d_u, l.ld_u, l.x, l.d_dv, l.ld_dv, ti * l.P, l.P, l.C, l.hd, add);
+        }
+    }
+    hipGraphExec_t exec = nullptr;
+    if (!st) {
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) st = hip_fail(e);
+    }
+    sdm_gx_graph* g = nullptr;
+    if (!st) {
+        g = new (std::nothrow) sdm_gx_graph;
+        if (!g) st = SDM_GX_ERR_HIP;
+    }
+    if (st) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(graph);
+        return st;
+    }
+    g->magic = kGraphMagic;
+    g->device = l.device;
+    g->nodes = nodes;
+    g->graph = graph;
+    g->exec = exec;
+    *out = g;
+    return SDM_GX_OK;
+}
+
+int sdm_gx_graph_launch(const sdm_gx_graph_t* graph, void* stream) {
+    if (!graph || graph->magic != kGraphMagic) return SDM_GX_ERR_PLAN;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev != graph->device) return SDM_GX_ERR_DEVICE;
+    e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDM_GX_OK : hip_fail(e);
+}
+
+int64_t sdm_gx_graph_nodes(const sdm_gx_graph_t* graph) {
+    return graph && graph->magic == kGraphMagic ? graph->nodes : -1;
+}
+
+int sdm_gx_graph_destroy(sdm_gx_graph_t* graph) {
+    if (!graph) return SDM_GX_OK;
+    if (graph->magic != kGraphMagic) return SDM_GX_ERR_PLAN;
+    hipError_t e1 = hipGraphExecDestroy(graph->exec);
+    hipError_t e2 = hipGraphDestroy(graph->graph);
+    graph->magic = 0;
+    delete graph;
+    if (e1 != hipSuccess) return hip_fail(e1);
+    if (e2 != hipSuccess) return hip_fail(e2);
+    return SDM_GX_OK;
 }
 
 int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]) {

@@ -27,9 +27,8 @@ struct KernelEntry {
     const void* fn;
 };
 
-// The kernel instance for (rows per wave, columns per lane, waves per workgroup, staging), or nullptr.
+// The kernel instance for (rows per wave, columns per lane, waves per workgroup, staging), or nullptr. Launched
+// with a 64 * waves thread block and one KernelArgs argument passed by value.
 const void* find_kernel(int ri, int rc, int waves, int stage);
-hipError_t launch_kernel(const void* fn, int waves, unsigned grid, unsigned lds_bytes, hipStream_t stream,
-                         const KernelArgs& a);
 
 }  // namespace sdm_gx

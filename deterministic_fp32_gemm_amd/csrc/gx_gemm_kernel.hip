@@ -358,10 +358,4 @@ const void* find_kernel(int ri, int rc, int waves, int stage) {
     return nullptr;
 }
 
-hipError_t launch_kernel(const void* fn, int waves, unsigned grid, unsigned lds_bytes, hipStream_t stream,
-                         const KernelArgs& a) {
-    void* args[] = {const_cast<KernelArgs*>(&a)};
-    return hipLaunchKernel(fn, dim3(grid), dim3(64u * static_cast<unsigned>(waves)), args, lds_bytes, stream);
-}
-
 }  // namespace sdm_gx

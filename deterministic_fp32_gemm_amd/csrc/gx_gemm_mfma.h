@@ -29,8 +29,8 @@ struct MfmaEntry {
     int lds_bytes;      // static LDS of the instance
 };
 
-// The kernel instance for the given shape parameters, or nullptr.
+// The kernel instance for the given shape parameters, or nullptr. Launched with a
+// 64 * (row_waves * col_waves + loader_waves) thread block and one MfmaArgs argument passed by value.
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves);
-hipError_t launch_mfma_kernel(const MfmaEntry& e, unsigned grid, hipStream_t stream, const MfmaArgs& a);
 
 }  // namespace sdm_gx

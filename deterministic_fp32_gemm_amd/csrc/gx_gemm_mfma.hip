@@ -284,10 +284,4 @@ const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int 
     return nullptr;
 }
 
-hipError_t launch_mfma_kernel(const MfmaEntry& e, unsigned grid, hipStream_t stream, const MfmaArgs& a) {
-    void* args[] = {const_cast<MfmaArgs*>(&a)};
-    const unsigned threads = 64u * static_cast<unsigned>(e.row_waves * e.col_waves + e.loader_waves);
-    return hipLaunchKernel(e.fn, dim3(grid), dim3(threads), args, 0, stream);
-}
-
 }  // namespace sdm_gx

@@ -30,7 +30,8 @@ def tensor_layout(d_u, x, d_dv):
 
 def make_step(d_u, x, d_dv, P: int, plan=None):
     """step(ti, stream=None) for 0 <= ti < N // P, plus step.fused(ti_begin, ti_end) (one launch for a range of
-    steps), step.prepared (the sdm_gx_launch_t) and step.geom (the plans). Everything is validated here, once."""
+    steps), step.graph(ti_begin, ti_end, mode) (a replayable HIP graph of that range), step.prepared (the
+    sdm_gx_launch_t) and step.geom (the plans). Everything is validated here, once."""
     N, C, hd, ld_u, ld_dv = tensor_layout(d_u, x, d_dv)
     P = int(P)
     if not 1 <= P <= N:
@@ -47,7 +48,12 @@ def make_step(d_u, x, d_dv, P: int, plan=None):
     def fused(ti_begin: int, ti_end: int, stream=None) -> None:
         B.sdm_gx_launch_fused(prepared, int(ti_begin), int(ti_end), stream)
 
+    def graph(ti_begin: int = 0, ti_end: int = lim, mode=B.SDM_GX_STEPS_FUSED) -> B.Graph:
+        """A HIP graph of steps ti_begin .. ti_end - 1 (per-step nodes or the fused launch), replayed with .launch()."""
+        return B.Graph(prepared, ti_begin, ti_end, mode)
+
     step.fused = fused
+    step.graph = graph
     step.prepared = prepared
     step.steps = lim
     step.geom = dict(step=prepared.plan_step.as_dict(), fused=prepared.plan_fused.as_dict())

@@ -191,6 +191,23 @@ SDM_GX_API int sdm_gx_launch(const sdm_gx_launch_t* prepared, int64_t ti, void* 
 /* Issue steps ti_begin .. ti_end - 1 of a prepared launch as ONE launch (every ti <= ti_max). */
 SDM_GX_API int sdm_gx_launch_fused(const sdm_gx_launch_t* prepared, int64_t ti_begin, int64_t ti_end, void* stream);
 
+/* A HIP graph of a prepared step range (the page's plan replay: the whole multi-step sequence captured once, then
+ * issued with one call). Kernel nodes are added explicitly, in issue order, each depending on the previous one:
+ *   SDM_GX_STEPS_FORWARD / SDM_GX_STEPS_REVERSE  one node per step launch (plan_step), ti ascending / descending
+ *   SDM_GX_STEPS_FUSED                           the fused launch of the range (plan_fused)
+ * The graph holds no memory of its own beyond the runtime's graph objects; it refers to the prepared launch's three
+ * buffers, which must outlive it. Replays are in-place updates like any launch (each replay adds the update again).
+ * ti_begin == ti_end gives an empty graph; launching it does nothing. The caller owns the graph and releases it with
+ * sdm_gx_graph_destroy (NULL is accepted). */
+typedef struct sdm_gx_graph sdm_gx_graph_t;
+SDM_GX_API int sdm_gx_graph_create(sdm_gx_graph_t** out, const sdm_gx_launch_t* prepared, int64_t ti_begin,
+                                   int64_t ti_end, int32_t mode);
+/* Replay the graph on `stream` (the current device must be the prepared one). */
+SDM_GX_API int sdm_gx_graph_launch(const sdm_gx_graph_t* graph, void* stream);
+/* Kernel nodes in the graph; -1 for an invalid handle. */
+SDM_GX_API int64_t sdm_gx_graph_nodes(const sdm_gx_graph_t* graph);
+SDM_GX_API int sdm_gx_graph_destroy(sdm_gx_graph_t* graph);
+
 /* Resource usage of the kernel instance a plan selects (the page's gx_gemm_attrs): out[0] VGPRs per lane,
  * out[1] private (scratch) bytes per lane, out[2] static LDS bytes, out[3] max threads per workgroup,
  * out[4] the plan's dynamic LDS bytes. Needs a device. */

@@ -231,3 +231,18 @@ def test_tensor_layout_rejects_bad_shapes():
         tensor_layout(du, x.transpose(1, 2), dv)
     with pytest.raises(ValueError):
         tensor_layout(du, x, torch.zeros(31, 10))
+
+
+def test_graph_entry_points_reject_bad_handles_without_a_device():
+    """Graph calls check their arguments before any HIP call."""
+    lib = g.load()
+    h = ctypes.c_void_p()
+    bad = g.sdm_gx_launch_t()                                        # no magic: not a prepared launch
+    assert lib.sdm_gx_graph_create(None, ctypes.byref(bad), 0, 1, 2) == g.SDM_GX_ERR_ARG
+    assert lib.sdm_gx_graph_create(ctypes.byref(h), ctypes.byref(bad), 0, 1, 7) == g.SDM_GX_ERR_ARG
+    assert lib.sdm_gx_graph_create(ctypes.byref(h), ctypes.byref(bad), 0, 1, 2) == g.SDM_GX_ERR_PLAN
+    assert lib.sdm_gx_graph_create(ctypes.byref(h), None, 0, 1, 2) == g.SDM_GX_ERR_PLAN
+    assert not h.value
+    assert lib.sdm_gx_graph_launch(None, None) == g.SDM_GX_ERR_PLAN
+    assert lib.sdm_gx_graph_nodes(None) == -1
+    assert lib.sdm_gx_graph_destroy(None) == g.SDM_GX_OK

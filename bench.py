@@ -37,7 +37,8 @@ def kernel_hash() -> str:
 
 
 PLAN_KEYS = ("engine", "rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows",
-             "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups")
+             "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups",
+             "mf_du_at_end")
 
 
 def kernel_name(plan: dict) -> str:
@@ -73,7 +74,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--plan", default=None,
                     help="override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,REG_SLABS,"
-                         "LOADER_WAVES[,WORKGROUPS]")
+                         "LOADER_WAVES[,WORKGROUPS[,DU_AT_END]]")
     return ap.parse_args()
 
 

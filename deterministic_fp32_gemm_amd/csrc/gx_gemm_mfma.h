@@ -24,13 +24,14 @@ struct MfmaArgs {
 };
 
 struct MfmaEntry {
-    int row_waves, col_waves, stages, reg_slabs, loader_waves;
+    int row_waves, col_waves, stages, reg_slabs, loader_waves, du_at_end;
     const void* fn;
     int lds_bytes;      // static LDS of the instance
 };
 
 // The kernel instance for the given shape parameters, or nullptr. Launched with a
 // 64 * (row_waves * col_waves + loader_waves) thread block and one MfmaArgs argument passed by value.
-const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves);
+const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
+                                  int du_at_end);
 
 }  // namespace sdm_gx

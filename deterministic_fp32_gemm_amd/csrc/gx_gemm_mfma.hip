@@ -24,8 +24,10 @@
 //     while the MFMAs of the current group issue. Rows past C are filled with x = -0 and d_dv = +0: their product is
 //     -0 and acc + (-0) == acc for every acc (including +-0, Inf and NaN), so a partial last slab runs the full 16
 //     steps without changing a bit.
-//   * d_u of an item is prefetched by the compute wavefronts when the item starts (accumulator layout, buffer loads
-//     with a scalar row offset) and d_u + acc is stored at the end of the item (one rounding).
+//   * d_u of an item is read by the compute wavefronts in accumulator layout (buffer loads with a scalar row offset)
+//     and d_u + acc is stored at the end of the item (one rounding). DU_AT_END = 0 prefetches it when the item
+//     starts; DU_AT_END = 1 reads it at the end, which saves 32 registers per lane: those instances are built for
+//     6 wavefronts per SIMD (MINW), so two workgroups share a compute unit and overlap each other's phases.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,8 +90,8 @@ struct Cursor {
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
-template <int RW, int QW, int S, int R, int LW>
-__global__ __launch_bounds__(64 * (RW * QW + LW)) void gx_mfma_kernel(const MfmaArgs a) {
+template <int RW, int QW, int S, int R, int LW, int DU_AT_END, int MINW>
+__global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_kernel(const MfmaArgs a) {
     constexpr int J = kSlabRows;
     constexpr int CWV = RW * QW, TLD = 64 * LW;
     constexpr int XW = 64 * RW, DW = 32 * QW;          // x / d_dv columns of a work item
@@ -221,17 +223,21 @@ __global__ __launch_bounds__(64 * (RW * QW + LW)) void gx_mfma_kernel(const Mfma
             const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(un, (short)0, C * ld4, kBufferFlags);
             const unsigned vo = static_cast<unsigned>(((i0 + 4 * h) * static_cast<int>(a.ld_u) + c) * 4);
             acc = (v32f){0};                             // the chain starts from +0
-            if (full) {
+            auto uload = [&]() {
+                if (full) {
 #pragma unroll
-                for (int r = 0; r < 32; ++r)
-                    u[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ur, vo, acc_row(r, 0) * ld4, 0));
-            } else {
+                    for (int r = 0; r < 32; ++r)
+                        u[r] = __builtin_bit_cast(float,
+                                                  __builtin_amdgcn_raw_buffer_load_b32(ur, vo, acc_row(r, 0) * ld4, 0));
+                } else {
 #pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    const int i = i0 + acc_row(r, h);
-                    u[r] = (i < C && c < hd) ? un[static_cast<int64_t>(i) * a.ld_u + c] : 0.f;
+                    for (int r = 0; r < 32; ++r) {
+                        const int i = i0 + acc_row(r, h);
+                        u[r] = (i < C && c < hd) ? un[static_cast<int64_t>(i) * a.ld_u + c] : 0.f;
+                    }
                 }
-            }
+            };
+            if (!DU_AT_END) uload();
             for (int s0 = 0; s0 < nsp; s0 += U) {
 #pragma unroll
                 for (int d = 0; d < U; ++d) {
@@ -240,6 +246,7 @@ __global__ __launch_bounds__(64 * (RW * QW + LW)) void gx_mfma_kernel(const Mfma
                     if (q < total) __syncthreads();
                 }
             }
+            if (DU_AT_END) uload();
             if (full) {
 #pragma unroll
                 for (int r = 0; r < 32; ++r)
@@ -259,11 +266,13 @@ __global__ __launch_bounds__(64 * (RW * QW + LW)) void gx_mfma_kernel(const Mfma
 
 // ---- instance table -----------------------------------------------------------------------------------------------
 // (row waves, column waves) tiles from 64x32 to 128x128 and 64x256 per item; S = 4 LDS stages; R = 2 or 4 register
-// slabs; 2 or 4 loader wavefronts. Left out: the combinations whose loader ring does not fit the registers that the
-// workgroup size allows (they spill): 64x256 and 128x128 tiles with 2 loader wavefronts and 4 register slabs.
-#define SDM_GX_MF(RW, QW, S, R, LW) \
-    {RW, QW, S, R, LW, reinterpret_cast<const void*>(&gx_mfma_kernel<RW, QW, S, R, LW>), \
+// slabs; 2 or 4 loader wavefronts; d_u prefetched at the item's start. Left out: the combinations whose loader ring
+// does not fit the registers that the workgroup size allows (they spill): 64x256 and 128x128 tiles with 2 loader
+// wavefronts and 4 register slabs. Two instances read d_u at the item's end and are built for two workgroups per CU.
+#define SDM_GX_MF_X(RW, QW, S, R, LW, DE, MW) \
+    {RW, QW, S, R, LW, DE, reinterpret_cast<const void*>(&gx_mfma_kernel<RW, QW, S, R, LW, DE, MW>), \
      static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW))},
+#define SDM_GX_MF(RW, QW, S, R, LW) SDM_GX_MF_X(RW, QW, S, R, LW, 0, 1)
 #define SDM_GX_MF_RL(RW, QW) SDM_GX_MF(RW, QW, 4, 4, 4) SDM_GX_MF(RW, QW, 4, 2, 4) SDM_GX_MF(RW, QW, 4, 4, 2) \
     SDM_GX_MF(RW, QW, 4, 2, 2)
 
@@ -272,14 +281,16 @@ const MfmaEntry kMfmaTable[] = {
     SDM_GX_MF(1, 8, 4, 4, 4) SDM_GX_MF(1, 8, 4, 2, 4) SDM_GX_MF(1, 8, 4, 2, 2)
     SDM_GX_MF_RL(2, 1) SDM_GX_MF_RL(2, 2)
     SDM_GX_MF(2, 4, 4, 4, 4) SDM_GX_MF(2, 4, 4, 2, 4) SDM_GX_MF(2, 4, 4, 2, 2)
+    SDM_GX_MF_X(2, 4, 4, 2, 4, 1, 6) SDM_GX_MF_X(1, 4, 4, 2, 4, 1, 6)
 };
 
 }  // namespace
 
-const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves) {
+const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
+                                  int du_at_end) {
     for (const MfmaEntry& e : kMfmaTable)
         if (e.row_waves == row_waves && e.col_waves == col_waves && e.stages == stages && e.reg_slabs == reg_slabs &&
-            e.loader_waves == loader_waves)
+            e.loader_waves == loader_waves && e.du_at_end == du_at_end)
             return &e;
     return nullptr;
 }

@@ -100,6 +100,9 @@ typedef enum sdm_gx_status {
  *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4)
  *   mf_loader_waves  loader wavefronts per workgroup (2 or 4; 4 with 4 register slabs for 64x256 and 128x128 items)
  *   mf_workgroups    workgroups to launch (0: one per compute unit); each takes a contiguous range of work items
+ *   mf_du_at_end     0: d_u prefetched when a work item starts; 1: read at its end (fewer registers: two workgroups
+ *                    fit one compute unit; instances for 128x128 and 64x128 items with 2 register slabs and 4
+ *                    loader wavefronts)
  * Outputs of the planner / sdm_gx_plan_complete:
  *   lds_bytes      LDS bytes per workgroup (dynamic for the VALU engine, static for the MFMA engine)
  *   wgs_per_cu     workgroups per CU that can be resident (0 if not known)
@@ -120,7 +123,7 @@ typedef struct sdm_gx_plan {
     int32_t mf_workgroups;
     int32_t lds_bytes;
     int32_t wgs_per_cu;
-    int32_t reserved;
+    int32_t mf_du_at_end;
     int64_t grid;
 } sdm_gx_plan_t;
 

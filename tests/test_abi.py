@@ -55,7 +55,7 @@ int main(void) {
          sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
          offsetof(sdm_gx_launch_t, plan_fused), offsetof(sdm_gx_plan_t, slab_rows),
          offsetof(sdm_gx_plan_t, mf_row_waves), offsetof(sdm_gx_plan_t, mf_workgroups),
-         offsetof(sdm_gx_plan_t, lds_bytes));
+         offsetof(sdm_gx_plan_t, mf_du_at_end));
   return 0;
 }
 """)
@@ -66,7 +66,7 @@ int main(void) {
                     g.sdm_gx_launch_t.ti_max.offset, g.sdm_gx_launch_t.plan_step.offset,
                     g.sdm_gx_launch_t.plan_fused.offset, g.sdm_gx_plan_t.slab_rows.offset,
                     g.sdm_gx_plan_t.mf_row_waves.offset, g.sdm_gx_plan_t.mf_workgroups.offset,
-                    g.sdm_gx_plan_t.lds_bytes.offset]
+                    g.sdm_gx_plan_t.mf_du_at_end.offset]
 
 
 def test_strerror_covers_every_code():
@@ -146,10 +146,12 @@ def test_plan_for_emits_supported_plans():
             if p.engine == g.SDM_GX_ENGINE_MFMA:
                 assert p.mf_row_waves == (2 if C > 64 else 1)
                 assert p.mf_col_waves == (4 if cdiv(hd, 32) > 2 else cdiv(hd, 32))
-                assert (p.mf_stages, p.mf_reg_slabs) == (4, 4) and p.mf_workgroups == 256
+                big = (p.mf_row_waves, p.mf_col_waves) == (2, 4)      # 128 x 128 items: two workgroups per CU
+                assert p.mf_stages == 4 and p.mf_reg_slabs == (2 if big else 4)
+                assert p.mf_du_at_end == (1 if big else 0) and p.mf_workgroups == (512 if big else 256)
                 assert p.mf_loader_waves == (2 if p.mf_row_waves * p.mf_col_waves <= 2 else 4)
                 items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 32 * p.mf_col_waves)
-                assert p.grid == mfma_grid(items)
+                assert p.grid == mfma_grid(items, p.mf_workgroups)
                 assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 8 * p.mf_col_waves)
                 continue
             assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
@@ -182,6 +184,8 @@ def test_plan_complete_rejects(bad):
     dict(mf_loader_waves=1), dict(mf_loader_waves=8), dict(mf_workgroups=-1),
     dict(mf_col_waves=8, mf_reg_slabs=4, mf_loader_waves=2),        # left out of the table: it spills
     dict(mf_row_waves=2, mf_col_waves=4, mf_reg_slabs=4, mf_loader_waves=2),
+    dict(mf_du_at_end=2), dict(mf_du_at_end=1),                       # d_u at the end: only 2 reg slabs, 4 loaders
+    dict(mf_du_at_end=1, mf_reg_slabs=2, mf_loader_waves=2),
 ])
 def test_mfma_plan_complete_rejects(bad):
     p = g.make_mfma_plan(1, 4)
@@ -191,14 +195,15 @@ def test_mfma_plan_complete_rejects(bad):
         g.sdm_gx_plan_complete(p, 4, 64, 64)
 
 
-MFMA_INSTANCES = [(rw, cw, rs, lw) for rw in (1, 2) for cw in (1, 2, 4, 8) for rs in (2, 4) for lw in (2, 4)
-                  if not (rw == 2 and cw == 8) and (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))]
+MFMA_INSTANCES = [(rw, cw, rs, lw, 0) for rw in (1, 2) for cw in (1, 2, 4, 8) for rs in (2, 4) for lw in (2, 4)
+                  if not (rw == 2 and cw == 8) and (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
+                 [(2, 4, 2, 4, 1), (1, 4, 2, 4, 1)]
 
 
-@pytest.mark.parametrize("rw,cw,rs,lw", MFMA_INSTANCES)
-def test_mfma_plan_complete_geometry(rw, cw, rs, lw):
+@pytest.mark.parametrize("rw,cw,rs,lw,de", MFMA_INSTANCES)
+def test_mfma_plan_complete_geometry(rw, cw, rs, lw, de):
     for nchunks, C, hd, wgs in ((512, 128, 128, 0), (7, 200, 33, 3), (1, 1, 1, 0), (1000, 64, 256, 100), (0, 64, 64, 0)):
-        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, 4, rs, lw, wgs), nchunks, C, hd)
+        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, 4, rs, lw, wgs, de), nchunks, C, hd)
         items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, 32 * cw)
         assert p.grid == mfma_grid(items, wgs or 256)
         assert p.lds_bytes == 16 * 4 * 16 * (16 * rw + 8 * cw)

@@ -106,13 +106,14 @@ def all_plans(C, hd=64):
         for cw in (1, 2, 4, 8):
             for rs in (2, 4):
                 for lw in (2, 4):
-                    for wgs in (0, 2):
-                        plan = g.make_mfma_plan(rw, cw, 4, rs, lw, wgs)
-                        try:
-                            g.sdm_gx_plan_complete(plan, 1, C, hd)
-                        except ValueError:
-                            continue
-                        yield plan
+                    for de in (0, 1):
+                        for wgs in (0, 2):
+                            plan = g.make_mfma_plan(rw, cw, 4, rs, lw, wgs, de)
+                            try:
+                                g.sdm_gx_plan_complete(plan, 1, C, hd)
+                            except ValueError:
+                                continue
+                            yield plan
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8)])
@@ -182,7 +183,8 @@ def test_mfma_engine_many_items_per_workgroup():
     case = DeviceCase(x, dv, du, hd, res_u=4, res_v=0, res_x=8)
     want = expected(x, dv, du, hd, 0, N)
     for plan in (g.make_mfma_plan(2, 2, 4, 4, 4, 3), g.make_mfma_plan(1, 1, 4, 2, 2, 7),
-                 g.make_mfma_plan(1, 8, 4, 2, 2, 1), g.make_mfma_plan(2, 4, 4, 4, 4, 0)):
+                 g.make_mfma_plan(1, 8, 4, 2, 2, 1), g.make_mfma_plan(2, 4, 4, 4, 4, 0),
+                 g.make_mfma_plan(2, 4, 4, 2, 4, 5, 1), g.make_mfma_plan(1, 4, 4, 2, 4, 0, 1)):
         for mode in (g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_FUSED):
             case.reset()
             say(f"mfma items plan {plan} mode {mode}")
@@ -304,7 +306,7 @@ def test_no_kernel_instance_spills():
     for plan in all_plans(256, 4096):
         if plan.engine == g.SDM_GX_ENGINE_MFMA:
             key = ("mfma", plan.mf_row_waves, plan.mf_col_waves, plan.mf_stages, plan.mf_reg_slabs,
-                   plan.mf_loader_waves)
+                   plan.mf_loader_waves, plan.mf_du_at_end)
             waves = plan.mf_row_waves * plan.mf_col_waves + plan.mf_loader_waves
         else:
             key = ("valu", plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
@@ -315,7 +317,7 @@ def test_no_kernel_instance_spills():
         attrs = g.sdm_gx_kernel_attrs(plan)
         assert attrs["scratch_bytes"] == 0, (key, attrs)
         assert attrs["vgprs"] * -(-waves // 4) <= 512, (key, attrs)
-    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 26
+    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 28
 
 
 def test_kernel_attrs_report_no_scratch():

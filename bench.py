@@ -38,11 +38,13 @@ def kernel_hash() -> str:
 
 PLAN_KEYS = ("engine", "rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows",
              "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups",
-             "mf_du_at_end")
+             "mf_du_at_end", "mf_block")
 
 
 def kernel_name(plan: dict) -> str:
-    return "gx_mfma_kernel" if plan.get("engine") == 1 else "gx_chain_kernel"
+    if plan.get("engine") != 1:
+        return "gx_chain_kernel"
+    return "gx_mfma_dma_kernel" if plan.get("mf_reg_slabs") == 0 else "gx_mfma_kernel"
 
 
 def measured_traffic(workload_key: int, driver: str, plan: dict):

@@ -124,6 +124,12 @@ constexpr int kDefaultSlabBytes = 32 * 1024;
 
 constexpr int kDefaultCus = 256;                // MI355X
 
+// The matrix-core kernel instance of a plan (mf_block 0 means 32), or nullptr.
+const sdm_gx::MfmaEntry* find_mfma(const sdm_gx_plan_t& p) {
+    return sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages, p.mf_reg_slabs, p.mf_loader_waves,
+                                    p.mf_du_at_end, p.mf_block > 0 ? p.mf_block : 32);
+}
+
 // Geometry of the matrix-core engine for nchunks chunks: work items and the persistent grid.
 struct MfmaGeom {
     int64_t nrg, ncg, items, per, grid;
@@ -131,7 +137,7 @@ struct MfmaGeom {
 MfmaGeom mfma_geom(const sdm_gx_plan_t& p, int64_t nchunks, int64_t C, int64_t hd) {
     MfmaGeom g;
     g.nrg = cdiv(cdiv(C, 64), p.mf_row_waves);
-    g.ncg = cdiv(hd, 32 * p.mf_col_waves);
+    g.ncg = cdiv(hd, static_cast<int64_t>(p.mf_block > 0 ? p.mf_block : 32) * p.mf_col_waves);
     g.items = nchunks * g.nrg * g.ncg;
     const int64_t wg = p.mf_workgroups > 0 ? p.mf_workgroups : kDefaultCus;
     const int64_t g0 = g.items < wg ? g.items : wg;
@@ -145,8 +151,8 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
     if (nchunks < 0) return SDM_GX_ERR_ARG;
     if (p->engine == SDM_GX_ENGINE_MFMA) {
         if (p->mf_workgroups < 0) return SDM_GX_ERR_PLAN;
-        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p->mf_row_waves, p->mf_col_waves, p->mf_stages,
-                                                             p->mf_reg_slabs, p->mf_loader_waves, p->mf_du_at_end);
+        if (p->mf_block == 0) p->mf_block = 32;
+        const sdm_gx::MfmaEntry* e = find_mfma(*p);
         if (!e) return SDM_GX_ERR_PLAN;
         p->lds_bytes = e->lds_bytes;
         if (lds_limit > 0 && p->lds_bytes > lds_limit) return SDM_GX_ERR_LIMIT;
@@ -185,11 +191,12 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 // Engine: the matrix cores for chunks with 32 <= C and hd <= 128, where their streaming kernel measured fastest
 // (64x64, 64x128 and 128x128 chunks); the vector-ALU chain otherwise (narrow C, where 64-row MFMA tiles would be
 // mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
-//  Matrix cores: one work item per chunk when it is at most 128 x 128 (row waves ceil(C/64) <= 2, column waves
-//  ceil(hd/32) <= 4), 4 LDS stages, 4 register slabs, 4 loader wavefronts (2 for items of 1 or 2 compute
-//  wavefronts), one persistent workgroup per compute unit. For 128 x 128 items: d_u read at the item's end and 2
-//  register slabs, the low-register instance that lets two workgroups share a compute unit, with two per unit
-//  (measured 10% faster on 128 x 128 chunks than one workgroup per unit walking two items).
+//  Matrix cores: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the
+//  32-column MFMA) with slabs moved straight to LDS (4 stages, 1 loader wavefront); work items of 64 or 128 rows
+//  (C <= 64 or not) by 64 columns (32 when hd <= 32); enough workgroups for 8 compute wavefronts per compute unit
+//  (two per unit for 64-row items). Measured against the register-ring instances: 13-15% faster on 64x128 and
+//  128x128 chunks, level on 64x64 chunks. A launch whose rows are not 16-byte aligned runs the same items through
+//  the register ring.
 //  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
@@ -210,17 +217,13 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
     if (allow_mfma && C >= 32 && hd <= 128) {
         sdm_gx_plan_t p{};
         p.engine = SDM_GX_ENGINE_MFMA;
+        p.mf_block = 16;
         p.mf_row_waves = C > 64 ? 2 : 1;
-        p.mf_col_waves = static_cast<int32_t>(cdiv(hd, 32) > 2 ? 4 : cdiv(hd, 32));
+        p.mf_col_waves = hd > 32 ? 4 : 2;
         p.mf_stages = 4;
-        p.mf_reg_slabs = 4;
-        p.mf_loader_waves = p.mf_row_waves * p.mf_col_waves <= 2 ? 2 : 4;
-        p.mf_workgroups = num_cus;
-        if (p.mf_row_waves == 2 && p.mf_col_waves == 4) {   // 128 x 128 items: two workgroups per compute unit
-            p.mf_reg_slabs = 2;
-            p.mf_du_at_end = 1;
-            p.mf_workgroups = 2 * num_cus;
-        }
+        p.mf_reg_slabs = 0;
+        p.mf_loader_waves = 1;
+        p.mf_workgroups = (p.mf_row_waves * p.mf_col_waves < 8 ? 2 : 1) * num_cus;
         const int st = complete_plan(&p, nchunks, C, hd, lds_limit);
         if (st == SDM_GX_OK) {
             *out = p;
@@ -266,6 +269,13 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
 // The matrix-core engine addresses a chunk of d_u with 32-bit byte offsets.
 bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1) << 31); }
 
+// Direct-to-LDS slabs (mf_reg_slabs 0) move 16-byte groups and address a chunk of d_dv with 32-bit byte offsets:
+// x and d_dv rows must start on 16-byte boundaries.
+bool dma_layout_ok(const float* x, const float* dv, int64_t C, int64_t ld_dv) {
+    return reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0 && C % 4 == 0 &&
+           ld_dv % 4 == 0 && C * ld_dv * 4 < (int64_t(1) << 31);
+}
+
 // ---- launching ----------------------------------------------------------------------------------------------------
 // Chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan. Splits very large grids so that one
 // launch stays below 2^31 work-items.
@@ -288,11 +298,22 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
     if (nchunks <= 0) return SDM_GX_OK;
     LaunchRec r;
     if (p.engine == SDM_GX_ENGINE_MFMA) {
-        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages,
-                                                             p.mf_reg_slabs, p.mf_loader_waves, p.mf_du_at_end);
+        const sdm_gx::MfmaEntry* e = find_mfma(p);
         if (!e) return SDM_GX_ERR_PLAN;
         if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
-        const MfmaGeom g = mfma_geom(p, nchunks, C, hd);
+        sdm_gx_plan_t q = p;
+        if (e->reg_slabs == 0 && !dma_layout_ok(x, dv, C, ld_dv)) {
+            // slabs cannot go straight to LDS: the same work items through the register ring (32-column
+            // wavefronts: a mf_block 16 tile of 2k column wavefronts is k of them)
+            if (e->block == 16) q.mf_col_waves = e->col_waves / 2;
+            q.mf_block = 32;
+            q.mf_stages = 4;
+            q.mf_reg_slabs = 2;
+            q.mf_loader_waves = 4;
+            e = find_mfma(q);
+            if (!e) return SDM_GX_ERR_PLAN;
+        }
+        const MfmaGeom g = mfma_geom(q, nchunks, C, hd);
         if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
         r.mfma = true;
         r.fn = e->fn;
@@ -452,8 +473,7 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
     const void* fn;
     int threads, dyn_lds;
     if (out->engine == SDM_GX_ENGINE_MFMA) {
-        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(out->mf_row_waves, out->mf_col_waves, out->mf_stages,
-                                                             out->mf_reg_slabs, out->mf_loader_waves, out->mf_du_at_end);
+        const sdm_gx::MfmaEntry* e = find_mfma(*out);
         fn = e->fn;
         threads = 64 * (out->mf_row_waves * out->mf_col_waves + out->mf_loader_waves);
         dyn_lds = 0;
@@ -644,8 +664,7 @@ int sdm_gx_kernel_attrs(const sdm_gx_plan_t* plan, int64_t out[5]) {
     if (!plan || !out) return SDM_GX_ERR_ARG;
     const void* fn = nullptr;
     if (plan->engine == SDM_GX_ENGINE_MFMA) {
-        const sdm_gx::MfmaEntry* e = sdm_gx::find_mfma_kernel(plan->mf_row_waves, plan->mf_col_waves, plan->mf_stages,
-                                                             plan->mf_reg_slabs, plan->mf_loader_waves, plan->mf_du_at_end);
+        const sdm_gx::MfmaEntry* e = find_mfma(*plan);
         if (e) fn = e->fn;
     } else if (plan->engine == SDM_GX_ENGINE_VALU) {
         fn = sdm_gx::find_kernel(plan->rows_per_wave, plan->cols_per_lane, plan->waves_per_wg, plan->staging);

@@ -7,7 +7,8 @@
 namespace sdm_gx {
 
 // Work items are (chunk, row group, column group) tiles; workgroup b takes items b*per .. b*per + per - 1 of chunks
-// n_begin .. n_begin + n_items / (nrg * ncg) - 1.
+// n_begin .. n_begin + n_items / (nrg * ncg) - 1. Item order: column group fastest in the register-ring kernel,
+// chunk fastest in the direct-to-LDS kernel.
 struct MfmaArgs {
     float* du;
     const float* x;
@@ -20,18 +21,19 @@ struct MfmaArgs {
     int32_t C;
     int32_t hd;
     int32_t nrg;        // row groups per chunk: ceil(ceil(C / 64) / row_waves)
-    int32_t ncg;        // column groups per chunk: ceil(hd / (32 * col_waves))
+    int32_t ncg;        // column groups per chunk: ceil(hd / (block * col_waves))
 };
 
 struct MfmaEntry {
     int row_waves, col_waves, stages, reg_slabs, loader_waves, du_at_end;
     const void* fn;
     int lds_bytes;      // static LDS of the instance
+    int block;          // MFMA block: 32 (64x32 tile per compute wavefront) or 16 (64x16)
 };
 
 // The kernel instance for the given shape parameters, or nullptr. Launched with a
 // 64 * (row_waves * col_waves + loader_waves) thread block and one MfmaArgs argument passed by value.
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
-                                  int du_at_end);
+                                  int du_at_end, int block);
 
 }  // namespace sdm_gx

@@ -87,6 +87,29 @@ struct Cursor {
     }
 };
 
+// Work item cursor with the chunk fastest: item it = ((rg * ncg) + cg) * nch + n for the launch's nch chunks.
+// Workgroups b and b + nch / per (per items each) then walk the same chunks in step for different column groups;
+// workgroups are dealt to the 8 XCDs round-robin, so when nch / per is a multiple of 8 they share an XCD and its L2,
+// and a chunk's x (read by every column group) and d_dv (read by every row group) come from HBM once.
+struct ChunkCursor {
+    int n, rg, cg;
+    __device__ __forceinline__ void init(int it, int nch, int ncg) {
+        n = __builtin_amdgcn_readfirstlane(it % nch);
+        it /= nch;
+        cg = __builtin_amdgcn_readfirstlane(it % ncg);
+        rg = __builtin_amdgcn_readfirstlane(it / ncg);
+    }
+    __device__ __forceinline__ void next(int nch, int ncg) {
+        if (++n == nch) {
+            n = 0;
+            if (++cg == ncg) {
+                cg = 0;
+                ++rg;
+            }
+        }
+    }
+};
+
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
@@ -264,6 +287,238 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_kernel(cons
     }
 }
 
+// ---- direct-to-LDS variant ----------------------------------------------------------------------------------------
+// Same work items, compute wavefronts, LDS stage layout and d_u handling as gx_mfma_kernel, but the loader wavefronts
+// move each slab straight from memory into its LDS stage with buffer_load_dwordx4 ... lds (one instruction moves
+// 64 x 16 contiguous bytes of LDS; each lane names its own source). No register ring: up to S - 1 slabs are in
+// flight per workgroup at no register cost, so a compute unit keeps far more bytes in flight than the register ring
+// allows. Needs x and d_dv rows on 16-byte boundaries (checked on the host).
+//   * Slab q of the workgroup's stream goes to stage q % S. Tick q: the loader waits (vmcnt) until slab q has landed,
+//     everyone meets at barrier B_q, the compute wavefronts run slab q, and the loader issues slab q + S - 1 into
+//     stage (q - 1) % S, whose reads by the compute wavefronts ended before B_q.
+//   * Out-of-range sources are cut by the buffer bounds (the chunk's extent): nothing outside the chunk is read.
+//     Rows past C in a slab are never used: the last slab of an item runs only its C - 16*s chain steps, so no
+//     padding value has to be exact. Stale or zero LDS in columns past hd or rows past C only reaches outputs
+//     that are never stored.
+//   * The loader meets the barriers with a bare s_barrier (the compute side's barrier would make the compiler wait
+//     for every load in flight); an empty asm with a memory clobber keeps the compiler from moving memory
+//     operations across it.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (lds wave-uniform)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, float* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {     // s_waitcnt vmcnt(N), other counters unconstrained
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// vmcnt(ahead * PERW) for a runtime ahead in [0, A]
+template <int PERW, int A>
+__device__ __forceinline__ void wait_slabs(int ahead) {
+    if constexpr (A == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= A) wait_vmcnt<A * PERW>();
+        else wait_slabs<PERW, A - 1>(ahead);
+    }
+}
+
+__device__ __forceinline__ void loader_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The two K = 1 FP32 MFMA shapes a compute wavefront can run the chain on; both give a 64-row output tile (lane l
+// supplies A = x[n, j, i0 + l]).
+//   32: v_mfma_f32_32x32x1_2b_f32, 64 rows x 32 columns, B = d_dv[n, j, c0 + l % 32], 64 cycles per step.
+//   16: v_mfma_f32_16x16x1_4b_f32, 64 rows x 16 columns, B = d_dv[n, j, c0 + l % 16], 32 cycles per step. Four
+//       16x16 blocks; register r holds block r/4 (rows 16*(r/4) ..), row 4*(l/16) + r%4 of it, column l % 16.
+template <int MS> struct MfShape;
+template <> struct MfShape<32> {
+    typedef v32f acc_t;
+    static constexpr int NR = 32;
+    __device__ static __forceinline__ acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ constexpr int row(int r) { return acc_row(r, 0); }
+    __device__ static __forceinline__ int lane_row(int lane) { return 4 * (lane >> 5); }
+};
+template <> struct MfShape<16> {
+    typedef float acc_t __attribute__((ext_vector_type(16)));
+    static constexpr int NR = 16;
+    __device__ static __forceinline__ acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ constexpr int row(int r) { return 16 * (r >> 2) + (r & 3); }
+    __device__ static __forceinline__ int lane_row(int lane) { return 4 * (lane >> 4); }
+};
+
+template <int RW, int QW, int S, int LW, int DU_AT_END, int MINW, int MS>
+__global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(const MfmaArgs a) {
+    typedef MfShape<MS> M;
+    typedef typename M::acc_t acc_t;
+    constexpr int NR = M::NR;
+    constexpr int J = kSlabRows;
+    constexpr int CWV = RW * QW;
+    constexpr int XW = 64 * RW, DW = MS * QW;          // x / d_dv columns of a work item
+    constexpr int GX = XW / 4, GD = DW / 4, GS = J * (GX + GD);   // float4 groups of one slab
+    constexpr int NI = GS / 64, NIX = J * GX / 64;      // DMA instructions per slab, of which x
+    constexpr int PERW = NI / LW;                       // per loader wavefront per slab
+    constexpr int K = kOperandGroup;
+    static_assert((S & (S - 1)) == 0 && S >= 2, "S: power of two");
+    static_assert(NIX % LW == 0 && (NI - NIX) % LW == 0, "loader wavefronts split x and d_dv evenly");
+    static_assert((S - 2) * PERW <= 63, "slabs in flight exceed the vmcnt range");
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int C = a.C, hd = a.hd;
+    const int first = static_cast<int>(blockIdx.x) * a.per;          // < n_items < 2^31
+    const int left = a.n_items - first;
+    const int nmine = left < a.per ? left : a.per;
+    if (nmine <= 0) return;                             // workgroup-uniform: no barrier reached
+    const int ns = (C + J - 1) / J;                     // slabs per item
+    const int nch = a.n_items / (a.nrg * a.ncg);        // chunks of the launch
+    const int64_t total = static_cast<int64_t>(nmine) * ns;
+
+    __shared__ f32x4a ring[S][GS];
+
+    if (wave >= CWV) {
+        const int wl = wave - CWV;
+        // instruction k of this wavefront is slab instruction m = wl + k*LW: x for k < NIX/LW, d_dv after;
+        // lane offsets within the slab (floats) do not depend on the slab
+        int off[PERW];
+#pragma unroll
+        for (int k = 0; k < PERW; ++k) {
+            const int m = wl + k * LW;
+            if (k < NIX / LW) {
+                const int g = m * 64 + lane, jj = g / GX;
+                off[k] = jj * C + (g - jj * GX) * 4;
+            } else {
+                const int h = (m - NIX) * 64 + lane, jj = h / GD;
+                off[k] = jj * static_cast<int>(a.ld_dv) + (h - jj * GD) * 4;
+            }
+        }
+        ChunkCursor lc;
+        lc.init(first, nch, a.ncg);
+        int ls = 0;
+        auto issue = [&](int stage) {                   // slab ls of item lc into `stage`
+            const int64_t n = a.n_begin + lc.n;
+            const int xo = ls * J * C + lc.rg * XW;                      // first float of the slab in x's chunk
+            const int64_t dvo = static_cast<int64_t>(ls * J) * a.ld_dv + lc.cg * DW;
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.x) + n * C * C + xo, (short)0, (C * C - xo) * 4, kBufferFlags);
+            const int dv_end = static_cast<int>((static_cast<int64_t>(C - 1) * a.ld_dv + hd - dvo) * 4);
+            const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.dv) + n * C * a.ld_dv + dvo, (short)0, dv_end, kBufferFlags);
+            float* st = reinterpret_cast<float*>(&ring[stage][0]);
+#pragma unroll
+            for (int k = 0; k < PERW; ++k) {
+                float* dst = st + (wl + k * LW) * 256;
+                if (k < NIX / LW)
+                    load_lds16(xr, dst, off[k] * 4);
+                else
+                    load_lds16(dr, dst, off[k] * 4);
+            }
+            if (++ls == ns) {
+                ls = 0;
+                lc.next(nch, a.ncg);
+            }
+        };
+#pragma unroll
+        for (int m = 0; m < S - 1; ++m)
+            if (m < total) issue(m);
+        for (int64_t q = 0; q < total; ++q) {
+            const int64_t rest = total - 1 - q;         // slabs after q already issued: min(S - 2, rest)
+            wait_slabs<PERW, S - 2>(rest < S - 2 ? static_cast<int>(rest) : S - 2);
+            loader_barrier();                           // B_q: slab q is in LDS
+            if (q + S - 1 < total) issue(static_cast<int>((q + S - 1) & (S - 1)));
+        }
+    } else {
+        const int rw = wave / QW, qw = wave - (wave / QW) * QW;
+        const float* xs0 = reinterpret_cast<const float*>(&ring[0][0]) + rw * 64 + lane;
+        const float* ds0 = reinterpret_cast<const float*>(&ring[0][0]) + J * XW + qw * MS + (lane & (MS - 1));
+        constexpr int STAGE_FLOATS = GS * 4;
+        acc_t acc;
+        auto compute = [&](const float* xs, const float* ds) {   // 16 chain steps from one ring stage
+            float ra[2][K], rb[2][K];
+            auto rd = [&](int buf, int grp) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    ra[buf][k] = xs[(grp * K + k) * XW];
+                    rb[buf][k] = ds[(grp * K + k) * DW];
+                }
+            };
+            rd(0, 0);
+#pragma unroll
+            for (int grp = 0; grp < J / K; ++grp) {
+                if (grp + 1 < J / K) rd((grp + 1) & 1, grp + 1);   // next group's operands in flight ...
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < K; ++k)                        // ... while this group's chain steps issue
+                    acc = M::step(ra[grp & 1][k], rb[grp & 1][k], acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto compute_tail = [&](const float* xs, const float* ds, int nk) {   // the first nk < 16 chain steps
+            for (int k = 0; k < nk; ++k) acc = M::step(xs[k * XW], ds[k * DW], acc);
+        };
+        ChunkCursor cc;
+        cc.init(first, nch, a.ncg);
+        const int lr = M::lane_row(lane);
+        const int ld4 = static_cast<int>(a.ld_u) * 4;   // < 2^31 / C: checked on the host
+        int64_t q = 0;
+        float u[NR];
+        for (int t = 0; t < nmine; ++t) {
+            const int64_t n = a.n_begin + cc.n;
+            const int i0 = cc.rg * XW + rw * 64, c = cc.cg * DW + qw * MS + (lane & (MS - 1));
+            const bool full = i0 + 64 <= C && cc.cg * DW + qw * MS + MS <= hd;   // wave-uniform
+            float* un = a.du + n * C * a.ld_u;
+            const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(un, (short)0, C * ld4, kBufferFlags);
+            const unsigned vo = static_cast<unsigned>(((i0 + lr) * static_cast<int>(a.ld_u) + c) * 4);
+            acc = (acc_t){0};                            // the chain starts from +0
+            auto uload = [&]() {
+                if (full) {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r)
+                        u[r] = __builtin_bit_cast(float,
+                                                  __builtin_amdgcn_raw_buffer_load_b32(ur, vo, M::row(r) * ld4, 0));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const int i = i0 + M::row(r) + lr;
+                        u[r] = (i < C && c < hd) ? un[static_cast<int64_t>(i) * a.ld_u + c] : 0.f;
+                    }
+                }
+            };
+            if (!DU_AT_END) uload();
+            for (int s = 0; s < ns; ++s, ++q) {
+                __syncthreads();                        // B_q: slab q is in LDS
+                const int off = static_cast<int>(q & (S - 1)) * STAGE_FLOATS;
+                if (s * J + J <= C) compute(xs0 + off, ds0 + off);
+                else compute_tail(xs0 + off, ds0 + off, C - s * J);
+            }
+            if (DU_AT_END) uload();
+            if (full) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, u[r] + acc[r]), ur, vo,
+                                                          M::row(r) * ld4, 0);
+            } else {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const int i = i0 + M::row(r) + lr;
+                    if (i < C && c < hd) un[static_cast<int64_t>(i) * a.ld_u + c] = u[r] + acc[r];
+                }
+            }
+            cc.next(nch, a.ncg);
+        }
+    }
+}
+
 // ---- instance table -----------------------------------------------------------------------------------------------
 // (row waves, column waves) tiles from 64x32 to 128x128 and 64x256 per item; S = 4 LDS stages; R = 2 or 4 register
 // slabs; 2 or 4 loader wavefronts; d_u prefetched at the item's start. Left out: the combinations whose loader ring
@@ -271,12 +526,22 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_kernel(cons
 // wavefronts and 4 register slabs. Two instances read d_u at the item's end and are built for two workgroups per CU.
 #define SDM_GX_MF_X(RW, QW, S, R, LW, DE, MW) \
     {RW, QW, S, R, LW, DE, reinterpret_cast<const void*>(&gx_mfma_kernel<RW, QW, S, R, LW, DE, MW>), \
-     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW))},
+     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW)), 32},
 #define SDM_GX_MF(RW, QW, S, R, LW) SDM_GX_MF_X(RW, QW, S, R, LW, 0, 1)
 #define SDM_GX_MF_RL(RW, QW) SDM_GX_MF(RW, QW, 4, 4, 4) SDM_GX_MF(RW, QW, 4, 2, 4) SDM_GX_MF(RW, QW, 4, 4, 2) \
     SDM_GX_MF(RW, QW, 4, 2, 2)
 
+// Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages and 1 loader wavefront, and with S = 8 and
+// 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two workgroups per CU.
+#define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS) \
+    {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS>), \
+     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + MS / 4 * QW)), MS},
+#define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS)
+
 const MfmaEntry kMfmaTable[] = {
+    SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)
+    SDM_GX_MD2(2, 2, 32) SDM_GX_MD2(2, 4, 32) SDM_GX_MD(2, 4, 4, 1, 1, 5, 32)
+    SDM_GX_MD2(1, 2, 16) SDM_GX_MD2(1, 4, 16) SDM_GX_MD2(1, 8, 16) SDM_GX_MD2(2, 2, 16) SDM_GX_MD2(2, 4, 16)
     SDM_GX_MF_RL(1, 1) SDM_GX_MF_RL(1, 2) SDM_GX_MF_RL(1, 4)
     SDM_GX_MF(1, 8, 4, 4, 4) SDM_GX_MF(1, 8, 4, 2, 4) SDM_GX_MF(1, 8, 4, 2, 2)
     SDM_GX_MF_RL(2, 1) SDM_GX_MF_RL(2, 2)
@@ -287,10 +552,10 @@ const MfmaEntry kMfmaTable[] = {
 }  // namespace
 
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
-                                  int du_at_end) {
+                                  int du_at_end, int block) {
     for (const MfmaEntry& e : kMfmaTable)
         if (e.row_waves == row_waves && e.col_waves == col_waves && e.stages == stages && e.reg_slabs == reg_slabs &&
-            e.loader_waves == loader_waves && e.du_at_end == du_at_end)
+            e.loader_waves == loader_waves && e.du_at_end == du_at_end && e.block == block)
             return &e;
     return nullptr;
 }

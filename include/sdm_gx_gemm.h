@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SDM_GX_ABI_VERSION 2
+#define SDM_GX_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define SDM_GX_API __attribute__((visibility("default")))
@@ -95,14 +95,28 @@ typedef enum sdm_gx_status {
  * SDM_GX_ENGINE_MFMA (persistent workgroups walking (chunk, row group, column group) work items; the other engine
  * ignores these fields):
  *   mf_row_waves     compute wavefronts along the rows of a work item, 64 rows each (1 or 2)
- *   mf_col_waves     compute wavefronts along its columns, 32 columns each (1, 2, 4, or 8 with mf_row_waves 1)
- *   mf_stages        LDS ring stages of 16 chain rows of x and d_dv (4)
- *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4)
- *   mf_loader_waves  loader wavefronts per workgroup (2 or 4; 4 with 4 register slabs for 64x256 and 128x128 items)
+ *   mf_col_waves     compute wavefronts along its columns, mf_block columns each (1, 2, 4, or 8 with mf_row_waves 1)
+ *   mf_stages        LDS ring stages of 16 chain rows of x and d_dv (4; 4 or 8 with mf_reg_slabs 0)
+ *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4), or 0: the
+ *                    loader wavefronts move slabs straight from memory into the LDS ring (buffer loads to LDS), up
+ *                    to mf_stages - 1 slabs in flight. That needs x and d_dv rows on 16-byte boundaries (x and d_dv
+ *                    16-byte aligned, C and ld_dv multiples of 4, C * ld_dv * 4 < 2^31); a launch whose pointers or
+ *                    strides do not allow it runs the same tiles through the register ring (2 register slabs,
+ *                    4 stages, 4 loader wavefronts), with the same results
+ *   mf_loader_waves  loader wavefronts per workgroup (2 or 4 with register slabs, 4 with 4 register slabs for 64x256
+ *                    and 128x128 items; with mf_reg_slabs 0: 1 with 4 stages, 2 with 8 stages)
  *   mf_workgroups    workgroups to launch (0: one per compute unit); each takes a contiguous range of work items
  *   mf_du_at_end     0: d_u prefetched when a work item starts; 1: read at its end (fewer registers: two workgroups
  *                    fit one compute unit; instances for 128x128 and 64x128 items with 2 register slabs and 4
- *                    loader wavefronts)
+ *                    loader wavefronts, and for 128x128 items with mf_reg_slabs 0, 4 stages, 1 loader wavefront)
+ *   mf_block         the MFMA that runs the chain, by output columns per compute wavefront (0 means 32):
+ *                    32: v_mfma_f32_32x32x1_2b_f32, a 64x32 tile per wavefront, 64 cycles per chain step;
+ *                    16: v_mfma_f32_16x16x1_4b_f32, a 64x16 tile, 32 cycles per step (half the chain latency of a
+ *                    work item, twice the wavefronts; mf_reg_slabs 0 only, tiles 64x32 .. 128x64 of mf_col_waves 2,
+ *                    4 or 8). Both are exact fma steps; the results do not depend on the choice. Where the layout
+ *                    rules out direct-to-LDS slabs, a mf_block 16 plan runs as mf_block 32 with half the column
+ *                    wavefronts (mf_col_waves 2 -> 1 ..), register slabs as above
+ *   reserved         0
  * Outputs of the planner / sdm_gx_plan_complete:
  *   lds_bytes      LDS bytes per workgroup (dynamic for the VALU engine, static for the MFMA engine)
  *   wgs_per_cu     workgroups per CU that can be resident (0 if not known)
@@ -124,6 +138,8 @@ typedef struct sdm_gx_plan {
     int32_t lds_bytes;
     int32_t wgs_per_cu;
     int32_t mf_du_at_end;
+    int32_t mf_block;
+    int32_t reserved;
     int64_t grid;
 } sdm_gx_plan_t;
 

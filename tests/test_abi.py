@@ -41,7 +41,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_abi_version():
-    assert g.sdm_gx_abi_version() == 2
+    assert g.sdm_gx_abi_version() == 3
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -51,11 +51,11 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "sdm_gx_gemm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
          sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
          offsetof(sdm_gx_launch_t, plan_fused), offsetof(sdm_gx_plan_t, slab_rows),
          offsetof(sdm_gx_plan_t, mf_row_waves), offsetof(sdm_gx_plan_t, mf_workgroups),
-         offsetof(sdm_gx_plan_t, mf_du_at_end));
+         offsetof(sdm_gx_plan_t, mf_du_at_end), offsetof(sdm_gx_plan_t, mf_block));
   return 0;
 }
 """)
@@ -66,7 +66,7 @@ int main(void) {
                     g.sdm_gx_launch_t.ti_max.offset, g.sdm_gx_launch_t.plan_step.offset,
                     g.sdm_gx_launch_t.plan_fused.offset, g.sdm_gx_plan_t.slab_rows.offset,
                     g.sdm_gx_plan_t.mf_row_waves.offset, g.sdm_gx_plan_t.mf_workgroups.offset,
-                    g.sdm_gx_plan_t.mf_du_at_end.offset]
+                    g.sdm_gx_plan_t.mf_du_at_end.offset, g.sdm_gx_plan_t.mf_block.offset]
 
 
 def test_strerror_covers_every_code():
@@ -144,15 +144,16 @@ def test_plan_for_emits_supported_plans():
             # engine rule: matrix cores for 32 <= C and hd <= 128
             assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and hd <= 128 else g.SDM_GX_ENGINE_VALU)
             if p.engine == g.SDM_GX_ENGINE_MFMA:
+                # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 (or 32) columns,
+                # 8 compute wavefronts per CU
+                assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 4 and p.mf_loader_waves == 1
                 assert p.mf_row_waves == (2 if C > 64 else 1)
-                assert p.mf_col_waves == (4 if cdiv(hd, 32) > 2 else cdiv(hd, 32))
-                big = (p.mf_row_waves, p.mf_col_waves) == (2, 4)      # 128 x 128 items: two workgroups per CU
-                assert p.mf_stages == 4 and p.mf_reg_slabs == (2 if big else 4)
-                assert p.mf_du_at_end == (1 if big else 0) and p.mf_workgroups == (512 if big else 256)
-                assert p.mf_loader_waves == (2 if p.mf_row_waves * p.mf_col_waves <= 2 else 4)
-                items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 32 * p.mf_col_waves)
+                assert p.mf_col_waves == (4 if hd > 32 else 2)
+                assert p.mf_du_at_end == 0
+                assert p.mf_workgroups == (512 if p.mf_row_waves * p.mf_col_waves < 8 else 256)
+                items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
-                assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 8 * p.mf_col_waves)
+                assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
                 continue
             assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
             assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
@@ -195,18 +196,49 @@ def test_mfma_plan_complete_rejects(bad):
         g.sdm_gx_plan_complete(p, 4, 64, 64)
 
 
-MFMA_INSTANCES = [(rw, cw, rs, lw, 0) for rw in (1, 2) for cw in (1, 2, 4, 8) for rs in (2, 4) for lw in (2, 4)
-                  if not (rw == 2 and cw == 8) and (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
-                 [(2, 4, 2, 4, 1), (1, 4, 2, 4, 1)]
+MFMA_TILES = [(rw, cw) for rw in (1, 2) for cw in (1, 2, 4, 8) if not (rw == 2 and cw == 8)]
+MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32) for rw, cw in MFMA_TILES for rs in (2, 4) for lw in (2, 4)
+                  if (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
+                 [(2, 4, 4, 2, 4, 1, 32), (1, 4, 4, 2, 4, 1, 32)] + \
+                 [(rw, cw, s, 0, lw, 0, 32) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
+                 [(2, 4, 4, 0, 1, 1, 32)] + \
+                 [(rw, cw, s, 0, lw, 0, 16) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
+                  for s, lw in ((4, 1), (8, 2))]
 
 
-@pytest.mark.parametrize("rw,cw,rs,lw,de", MFMA_INSTANCES)
-def test_mfma_plan_complete_geometry(rw, cw, rs, lw, de):
+@pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk", MFMA_INSTANCES)
+def test_mfma_plan_complete_geometry(rw, cw, s, rs, lw, de, blk):
     for nchunks, C, hd, wgs in ((512, 128, 128, 0), (7, 200, 33, 3), (1, 1, 1, 0), (1000, 64, 256, 100), (0, 64, 64, 0)):
-        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, 4, rs, lw, wgs, de), nchunks, C, hd)
-        items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, 32 * cw)
+        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, wgs, de, blk), nchunks, C, hd)
+        items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, blk * cw)
         assert p.grid == mfma_grid(items, wgs or 256)
-        assert p.lds_bytes == 16 * 4 * 16 * (16 * rw + 8 * cw)
+        assert p.lds_bytes == 16 * s * 16 * (16 * rw + blk // 4 * cw)
+        assert p.mf_block == blk
+
+
+def test_mfma_block_zero_means_32():
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 2, 4, 4, 2, 0, 0, 0), 8, 64, 64)
+    assert p.mf_block == 32 and p.grid == 8
+
+
+def test_mfma_direct_to_lds_fallback_instances_exist():
+    """A direct-to-LDS plan whose launch finds unaligned x or d_dv rows runs the same work items through the register
+    ring with 4 stages, 2 register slabs and 4 loader wavefronts of 32-column wavefronts (half as many column
+    wavefronts for a 16-column plan): that instance exists for every direct-to-LDS one."""
+    for rw, cw, s, rs, lw, de, blk in MFMA_INSTANCES:
+        if rs == 0:
+            fcw = cw // 2 if blk == 16 else cw
+            assert (rw, fcw, 4, 2, 4, de, 32) in MFMA_INSTANCES
+            g.sdm_gx_plan_complete(g.make_mfma_plan(rw, fcw, 4, 2, 4, 0, de), 4, 64, 64)
+
+
+def test_mfma_direct_to_lds_rejects_missing_instances():
+    for s, rs, lw in ((8, 0, 1), (4, 0, 2), (2, 0, 1), (8, 2, 4)):
+        with pytest.raises(ValueError):
+            g.sdm_gx_plan_complete(g.make_mfma_plan(2, 4, s, rs, lw), 4, 128, 128)
+    for rw, cw, s, rs, lw, blk in ((1, 1, 4, 0, 1, 16), (1, 2, 4, 4, 2, 16), (1, 2, 4, 0, 1, 8), (1, 2, 4, 0, 1, 64)):
+        with pytest.raises(ValueError):
+            g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, 0, 0, blk), 4, 64, 64)
 
 def test_plan_complete_rows_beyond_c():
     with pytest.raises(ValueError):

@@ -104,19 +104,29 @@ def all_plans(C, hd=64):
                             yield plan
     for rw in (1, 2):
         for cw in (1, 2, 4, 8):
-            for rs in (2, 4):
-                for lw in (2, 4):
-                    for de in (0, 1):
-                        for wgs in (0, 2):
-                            plan = g.make_mfma_plan(rw, cw, 4, rs, lw, wgs, de)
-                            try:
-                                g.sdm_gx_plan_complete(plan, 1, C, hd)
-                            except ValueError:
-                                continue
-                            yield plan
+            for stages, rs, lw, blk in ((4, 2, 2, 32), (4, 2, 4, 32), (4, 4, 2, 32), (4, 4, 4, 32), (4, 0, 1, 32),
+                                        (8, 0, 2, 32), (4, 0, 1, 16), (8, 0, 2, 16)):
+                for de in (0, 1):
+                    for wgs in (0, 2):
+                        plan = g.make_mfma_plan(rw, cw, stages, rs, lw, wgs, de, blk)
+                        try:
+                            g.sdm_gx_plan_complete(plan, 1, C, hd)
+                        except ValueError:
+                            continue
+                        yield plan
 
 
-@pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8)])
+def dma_plans():
+    """Matrix-core plans whose slabs go straight to LDS (mf_reg_slabs 0), several work items per workgroup."""
+    return [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0) for rw, cw in ((1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2),
+                                                                      (2, 4)) for s, lw, wgs in ((4, 1, 3), (8, 2, 0))] \
+        + [g.make_mfma_plan(2, 4, 4, 0, 1, 5, 1)] \
+        + [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0, 16) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
+           for s, lw, wgs in ((4, 1, 3), (8, 2, 0))]
+
+
+@pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8),
+                                        (100, 72, 76, 0), (36, 40, 44, 0)])
 def test_every_plan_is_bit_identical(C, hd, ld, res):
     N, P = 6, 3
     x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C + hd)
@@ -144,13 +154,15 @@ def test_signed_zero_through_padded_steps(C):
     du[:, :, hd:] = np.float32(3.5)                            # padding columns: must stay untouched
     want = expected(x, dv, du, hd, 0, N)
     assert (np.signbit(want[:, :, :hd])).all() and (want[:, :, :hd] == 0).all()
-    case = DeviceCase(x, dv, du, hd, res_u=4, res_v=8, res_x=12)
-    plans = [None, g.make_mfma_plan(1, 2, 4, 4, 2), g.make_mfma_plan(2, 1, 4, 2, 4, 1), g.make_plan(1, 1, 2, 1, 1)]
-    for plan in plans:
-        case.reset()
-        say(f"signed zero C={C} plan {plan}")
-        got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, plan)
-        assert_matches(got, want, du, hd, f"signed zero C={C} plan {plan}")
+    plans = [None, g.make_mfma_plan(1, 2, 4, 4, 2), g.make_mfma_plan(2, 1, 4, 2, 4, 1), g.make_plan(1, 1, 2, 1, 1),
+             g.make_mfma_plan(1, 2, 4, 0, 1), g.make_mfma_plan(2, 1, 8, 0, 2, 1)]
+    for res in ((4, 8, 12), (0, 0, 0)):             # direct-to-LDS slabs need the aligned layout
+        case = DeviceCase(x, dv, du, hd, res_u=res[0], res_v=res[1], res_x=res[2])
+        for plan in plans:
+            case.reset()
+            say(f"signed zero C={C} res {res} plan {plan}")
+            got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, plan)
+            assert_matches(got, want, du, hd, f"signed zero C={C} res {res} plan {plan}")
 
 
 def test_mfma_engine_single_rounding():
@@ -173,6 +185,24 @@ def test_mfma_engine_single_rounding():
     case = DeviceCase(x, dv, du, hd)
     got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, g.make_mfma_plan(1, 2, 4, 4, 2))
     assert_matches(got, want, du, hd, "mfma single rounding")
+
+
+@pytest.mark.parametrize("C,hd,ld,res", [(148, 70, 76, (0, 0, 0)), (64, 64, 64, (0, 0, 0)), (128, 128, 128, (4, 0, 0)),
+                                        (36, 100, 104, (0, 0, 0)), (64, 128, 131, (0, 4, 0)), (148, 70, 76, (0, 0, 8))])
+def test_mfma_direct_to_lds_plans(C, hd, ld, res):
+    """Slabs moved straight from memory into LDS (mf_reg_slabs 0): ragged rows, columns and last slabs (C % 16 != 0
+    runs only the chain's own steps), several items per workgroup, per step and fused. Where x or d_dv rows are not
+    16-byte aligned (d_dv at +4 B, ld 131, x at +8 B) the launch takes the register ring, with the same bits."""
+    N, P = 12, 4
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C * 3 + hd)
+    case = DeviceCase(x, dv, du, hd, res_u=res[0], res_v=res[1], res_x=res[2])
+    want = expected(x, dv, du, hd, 0, N)
+    for plan in dma_plans():
+        for mode in (g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_FUSED):
+            case.reset()
+            say(f"direct-to-LDS C={C} hd={hd} ld={ld} res={res} plan {plan} mode {mode}")
+            got = run_steps(case, P, 0, N // P, mode, plan)
+            assert_matches(got, want, du, hd, f"direct-to-LDS plan {plan} mode {mode}")
 
 
 def test_mfma_engine_many_items_per_workgroup():
@@ -306,7 +336,7 @@ def test_no_kernel_instance_spills():
     for plan in all_plans(256, 4096):
         if plan.engine == g.SDM_GX_ENGINE_MFMA:
             key = ("mfma", plan.mf_row_waves, plan.mf_col_waves, plan.mf_stages, plan.mf_reg_slabs,
-                   plan.mf_loader_waves, plan.mf_du_at_end)
+                   plan.mf_loader_waves, plan.mf_du_at_end, plan.mf_block)
             waves = plan.mf_row_waves * plan.mf_col_waves + plan.mf_loader_waves
         else:
             key = ("valu", plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
@@ -317,7 +347,7 @@ def test_no_kernel_instance_spills():
         attrs = g.sdm_gx_kernel_attrs(plan)
         assert attrs["scratch_bytes"] == 0, (key, attrs)
         assert attrs["vgprs"] * -(-waves // 4) <= 512, (key, attrs)
-    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 28
+    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 53
 
 
 def test_kernel_attrs_report_no_scratch():

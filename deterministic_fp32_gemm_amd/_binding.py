@@ -83,6 +83,8 @@ def lib_path() -> str:
 def load() -> ctypes.CDLL:
     """Load the HIP library (once). Fails loudly if it has not been built: there is no fallback path."""
     global _lib
+    if _lib is not None:                # loaded: no lock on the launch path
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -214,13 +216,13 @@ def make_plan(rows_per_wave, cols_per_lane, waves_per_wg, staging=0, xcd_remap=0
 
 
 def make_mfma_plan(row_waves, col_waves, stages=4, reg_slabs=4, loader_waves=4, workgroups=0,
-                   du_at_end=0, block=32) -> sdm_gx_plan_t:
+                   du_at_end=0, block=32, slab_rows=0) -> sdm_gx_plan_t:
     """A caller-made plan for the matrix-core engine (validated by the entry point that receives it)."""
     p = sdm_gx_plan_t()
     p.engine = SDM_GX_ENGINE_MFMA
     p.mf_row_waves, p.mf_col_waves, p.mf_stages = row_waves, col_waves, stages
     p.mf_reg_slabs, p.mf_loader_waves, p.mf_workgroups = reg_slabs, loader_waves, workgroups
-    p.mf_du_at_end, p.mf_block = du_at_end, block
+    p.mf_du_at_end, p.mf_block, p.slab_rows = du_at_end, block, slab_rows
     return p
 
 

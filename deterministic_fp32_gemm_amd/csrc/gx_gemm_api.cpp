@@ -124,10 +124,11 @@ constexpr int kDefaultSlabBytes = 32 * 1024;
 
 constexpr int kDefaultCus = 256;                // MI355X
 
-// The matrix-core kernel instance of a plan (mf_block 0 means 32), or nullptr.
+// The matrix-core kernel instance of a plan (mf_block 0 means 32, slab_rows 0 means 16), or nullptr.
 const sdm_gx::MfmaEntry* find_mfma(const sdm_gx_plan_t& p) {
     return sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages, p.mf_reg_slabs, p.mf_loader_waves,
-                                    p.mf_du_at_end, p.mf_block > 0 ? p.mf_block : 32);
+                                    p.mf_du_at_end, p.mf_block > 0 ? p.mf_block : 32,
+                                    p.slab_rows > 0 ? p.slab_rows : 16);
 }
 
 // Geometry of the matrix-core engine for nchunks chunks: work items and the persistent grid.
@@ -152,6 +153,7 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
     if (p->engine == SDM_GX_ENGINE_MFMA) {
         if (p->mf_workgroups < 0) return SDM_GX_ERR_PLAN;
         if (p->mf_block == 0) p->mf_block = 32;
+        if (p->slab_rows == 0) p->slab_rows = 16;
         const sdm_gx::MfmaEntry* e = find_mfma(*p);
         if (!e) return SDM_GX_ERR_PLAN;
         p->lds_bytes = e->lds_bytes;
@@ -193,10 +195,12 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 // mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
 //  Matrix cores: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the
 //  32-column MFMA) with slabs moved straight to LDS (4 stages, 1 loader wavefront); work items of 64 or 128 rows
-//  (C <= 64 or not) by 64 columns (32 when hd <= 32); enough workgroups for 8 compute wavefronts per compute unit
-//  (two per unit for 64-row items). Measured against the register-ring instances: 13-15% faster on 64x128 and
-//  128x128 chunks, level on 64x64 chunks. A launch whose rows are not 16-byte aligned runs the same items through
-//  the register ring.
+//  (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); enough
+//  workgroups for 8 compute wavefronts per compute unit (two per unit for 64x64 items). Stages of 32 chain rows
+//  when each CU holds one workgroup (half the barrier bubbles, which no other workgroup fills), 16 when it holds two
+//  (the chain starts on a smaller first slab). Measured against the register-ring instances with launches replayed
+//  from graphs: 39% faster on 64x64 chunks, 19% on 64x128, 18% on 128x128. A launch whose rows are not 16-byte
+//  aligned runs the same items through the register ring.
 //  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
@@ -220,11 +224,17 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
         p.mf_block = 16;
         p.mf_row_waves = C > 64 ? 2 : 1;
         p.mf_col_waves = hd > 32 ? 4 : 2;
+        if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
         p.mf_stages = 4;
         p.mf_reg_slabs = 0;
         p.mf_loader_waves = 1;
         p.mf_workgroups = (p.mf_row_waves * p.mf_col_waves < 8 ? 2 : 1) * num_cus;
-        const int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+        p.slab_rows = 16;
+        int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+        if (st == SDM_GX_OK && p.grid <= num_cus) {             // one workgroup per CU: 32-row stages
+            p.slab_rows = 32;
+            st = complete_plan(&p, nchunks, C, hd, lds_limit);
+        }
         if (st == SDM_GX_OK) {
             *out = p;
             return SDM_GX_OK;
@@ -307,6 +317,7 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
             // wavefronts: a mf_block 16 tile of 2k column wavefronts is k of them)
             if (e->block == 16) q.mf_col_waves = e->col_waves / 2;
             q.mf_block = 32;
+            q.slab_rows = 16;
             q.mf_stages = 4;
             q.mf_reg_slabs = 2;
             q.mf_loader_waves = 4;

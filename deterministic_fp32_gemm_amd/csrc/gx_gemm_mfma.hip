@@ -18,7 +18,7 @@
 //   * Compute wavefronts (RW x QW of them) each own one 64-row x 32-column output tile: two 32x32 MFMA blocks
 //     stacked along the rows. Lane l supplies A = x[n, j, i0 + l] and B = d_dv[n, j, c0 + l % 32].
 //   * Loader wavefronts (LW of them) stream the x and d_dv rows of all the workgroup's items, 16 chain rows ("a
-//     slab") at a time, with float4 loads into an R-deep register ring and from there into an S-stage LDS ring that
+//     slab"; 16 or 32 in the direct-to-LDS variant) at a time, with float4 loads into an R-deep register ring and from there into an S-stage LDS ring that
 //     runs S-1 slabs ahead of the compute wavefronts. One workgroup barrier per slab.
 //   * Compute wavefronts read their MFMA operands from the LDS ring, the next group of 4 chain rows always in flight
 //     while the MFMAs of the current group issue. Rows past C are filled with x = -0 and d_dv = +0: their product is
@@ -358,12 +358,11 @@ template <> struct MfShape<16> {
     __device__ static __forceinline__ int lane_row(int lane) { return 4 * (lane >> 4); }
 };
 
-template <int RW, int QW, int S, int LW, int DU_AT_END, int MINW, int MS>
+template <int RW, int QW, int S, int LW, int DU_AT_END, int MINW, int MS, int J>
 __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(const MfmaArgs a) {
     typedef MfShape<MS> M;
     typedef typename M::acc_t acc_t;
     constexpr int NR = M::NR;
-    constexpr int J = kSlabRows;
     constexpr int CWV = RW * QW;
     constexpr int XW = 64 * RW, DW = MS * QW;          // x / d_dv columns of a work item
     constexpr int GX = XW / 4, GD = DW / 4, GS = J * (GX + GD);   // float4 groups of one slab
@@ -526,22 +525,24 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 // wavefronts and 4 register slabs. Two instances read d_u at the item's end and are built for two workgroups per CU.
 #define SDM_GX_MF_X(RW, QW, S, R, LW, DE, MW) \
     {RW, QW, S, R, LW, DE, reinterpret_cast<const void*>(&gx_mfma_kernel<RW, QW, S, R, LW, DE, MW>), \
-     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW)), 32},
+     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW)), 32, kSlabRows},
 #define SDM_GX_MF(RW, QW, S, R, LW) SDM_GX_MF_X(RW, QW, S, R, LW, 0, 1)
 #define SDM_GX_MF_RL(RW, QW) SDM_GX_MF(RW, QW, 4, 4, 4) SDM_GX_MF(RW, QW, 4, 2, 4) SDM_GX_MF(RW, QW, 4, 4, 2) \
     SDM_GX_MF(RW, QW, 4, 2, 2)
 
-// Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages and 1 loader wavefront, and with S = 8 and
-// 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two workgroups per CU.
-#define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS) \
-    {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS>), \
-     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + MS / 4 * QW)), MS},
-#define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS)
+// Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages of 16 chain rows and 1 loader wavefront, and
+// with S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
+// workgroups per CU; the 16-column tiles also with 32-row stages (4 stages, 1 loader wavefront).
+#define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) \
+    {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J>), \
+     static_cast<int>(sizeof(f32x4a) * S * J * (16 * RW + MS / 4 * QW)), MS, J},
+#define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS, 16)
+#define SDM_GX_MD3(RW, QW) SDM_GX_MD2(RW, QW, 16) SDM_GX_MD(RW, QW, 4, 1, 0, 1, 16, 32)
 
 const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)
-    SDM_GX_MD2(2, 2, 32) SDM_GX_MD2(2, 4, 32) SDM_GX_MD(2, 4, 4, 1, 1, 5, 32)
-    SDM_GX_MD2(1, 2, 16) SDM_GX_MD2(1, 4, 16) SDM_GX_MD2(1, 8, 16) SDM_GX_MD2(2, 2, 16) SDM_GX_MD2(2, 4, 16)
+    SDM_GX_MD2(2, 2, 32) SDM_GX_MD2(2, 4, 32) SDM_GX_MD(2, 4, 4, 1, 1, 5, 32, 16)
+    SDM_GX_MD3(1, 2) SDM_GX_MD3(1, 4) SDM_GX_MD3(1, 8) SDM_GX_MD3(2, 2) SDM_GX_MD3(2, 4)
     SDM_GX_MF_RL(1, 1) SDM_GX_MF_RL(1, 2) SDM_GX_MF_RL(1, 4)
     SDM_GX_MF(1, 8, 4, 4, 4) SDM_GX_MF(1, 8, 4, 2, 4) SDM_GX_MF(1, 8, 4, 2, 2)
     SDM_GX_MF_RL(2, 1) SDM_GX_MF_RL(2, 2)
@@ -552,10 +553,11 @@ const MfmaEntry kMfmaTable[] = {
 }  // namespace
 
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
-                                  int du_at_end, int block) {
+                                  int du_at_end, int block, int slab_rows) {
     for (const MfmaEntry& e : kMfmaTable)
         if (e.row_waves == row_waves && e.col_waves == col_waves && e.stages == stages && e.reg_slabs == reg_slabs &&
-            e.loader_waves == loader_waves && e.du_at_end == du_at_end && e.block == block)
+            e.loader_waves == loader_waves && e.du_at_end == du_at_end && e.block == block &&
+            e.slab_rows == slab_rows)
             return &e;
     return nullptr;
 }

@@ -83,7 +83,7 @@ typedef enum sdm_gx_status {
 /* A launch plan: which engine runs the update and how output tiles map onto wavefronts and workgroups. Results
  * never depend on it.
  *   engine         SDM_GX_ENGINE_VALU or SDM_GX_ENGINE_MFMA
- * SDM_GX_ENGINE_VALU (the other engine ignores these fields):
+ * SDM_GX_ENGINE_VALU (the other engine ignores these fields, except slab_rows):
  *   rows_per_wave  RI: output rows one wavefront owns (1, 2, 4, 8 or 16; RI <= C)
  *   cols_per_lane  RC: adjacent output columns one lane owns (1, 2 or 4); a wavefront covers 64*RC columns
  *   waves_per_wg   wavefronts per workgroup (1, 2, 4, 8, or 16 for some tiles); they take consecutive row blocks of
@@ -91,12 +91,14 @@ typedef enum sdm_gx_status {
  *   staging        0: each wavefront reads its d_dv columns straight from global memory;
  *                  1: the workgroup stages its d_dv column block in LDS once and every wavefront reads it there
  *   xcd_remap      1: workgroup ids are permuted so that the workgroups of one chunk run on one XCD (one L2)
- *   slab_rows      staging 1: d_dv rows per LDS slab (0: the planner's choice; clamped to C)
+ *   slab_rows      staging 1: d_dv rows per LDS slab (0: the planner's choice; clamped to C). The MFMA engine reads
+ *                  it too: chain rows per LDS stage, 16 (0 means 16) or 32 (direct-to-LDS 16-column tiles with
+ *                  4 stages and 1 loader wavefront)
  * SDM_GX_ENGINE_MFMA (persistent workgroups walking (chunk, row group, column group) work items; the other engine
  * ignores these fields):
  *   mf_row_waves     compute wavefronts along the rows of a work item, 64 rows each (1 or 2)
  *   mf_col_waves     compute wavefronts along its columns, mf_block columns each (1, 2, 4, or 8 with mf_row_waves 1)
- *   mf_stages        LDS ring stages of 16 chain rows of x and d_dv (4; 4 or 8 with mf_reg_slabs 0)
+ *   mf_stages        LDS ring stages of slab_rows chain rows of x and d_dv (4; 4 or 8 with mf_reg_slabs 0)
  *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4), or 0: the
  *                    loader wavefronts move slabs straight from memory into the LDS ring (buffer loads to LDS), up
  *                    to mf_stages - 1 slabs in flight. That needs x and d_dv rows on 16-byte boundaries (x and d_dv

@@ -144,16 +144,19 @@ def test_plan_for_emits_supported_plans():
             # engine rule: matrix cores for 32 <= C and hd <= 128
             assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and hd <= 128 else g.SDM_GX_ENGINE_VALU)
             if p.engine == g.SDM_GX_ENGINE_MFMA:
-                # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 (or 32) columns,
-                # 8 compute wavefronts per CU
+                # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 columns (32 when hd <= 32
+                # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU, 32-row stages when
+                # each CU holds one workgroup
                 assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 4 and p.mf_loader_waves == 1
                 assert p.mf_row_waves == (2 if C > 64 else 1)
-                assert p.mf_col_waves == (4 if hd > 32 else 2)
+                wide = hd > 32 and nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) >= 256
+                assert p.mf_col_waves == (4 if wide else 2)
                 assert p.mf_du_at_end == 0
                 assert p.mf_workgroups == (512 if p.mf_row_waves * p.mf_col_waves < 8 else 256)
                 items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
-                assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
+                assert p.slab_rows == (32 if p.grid <= 256 else 16)
+                assert p.lds_bytes == 16 * 4 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
                 continue
             assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
             assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
@@ -197,38 +200,38 @@ def test_mfma_plan_complete_rejects(bad):
 
 
 MFMA_TILES = [(rw, cw) for rw in (1, 2) for cw in (1, 2, 4, 8) if not (rw == 2 and cw == 8)]
-MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32) for rw, cw in MFMA_TILES for rs in (2, 4) for lw in (2, 4)
+MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs in (2, 4) for lw in (2, 4)
                   if (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
-                 [(2, 4, 4, 2, 4, 1, 32), (1, 4, 4, 2, 4, 1, 32)] + \
-                 [(rw, cw, s, 0, lw, 0, 32) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
-                 [(2, 4, 4, 0, 1, 1, 32)] + \
-                 [(rw, cw, s, 0, lw, 0, 16) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-                  for s, lw in ((4, 1), (8, 2))]
+                 [(2, 4, 4, 2, 4, 1, 32, 16), (1, 4, 4, 2, 4, 1, 32, 16)] + \
+                 [(rw, cw, s, 0, lw, 0, 32, 16) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
+                 [(2, 4, 4, 0, 1, 1, 32, 16)] + \
+                 [(rw, cw, s, 0, lw, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
+                  for s, lw, j in ((4, 1, 16), (8, 2, 16), (4, 1, 32))]
 
 
-@pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk", MFMA_INSTANCES)
-def test_mfma_plan_complete_geometry(rw, cw, s, rs, lw, de, blk):
+@pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk,j", MFMA_INSTANCES)
+def test_mfma_plan_complete_geometry(rw, cw, s, rs, lw, de, blk, j):
     for nchunks, C, hd, wgs in ((512, 128, 128, 0), (7, 200, 33, 3), (1, 1, 1, 0), (1000, 64, 256, 100), (0, 64, 64, 0)):
-        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, wgs, de, blk), nchunks, C, hd)
+        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, wgs, de, blk, j), nchunks, C, hd)
         items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, blk * cw)
         assert p.grid == mfma_grid(items, wgs or 256)
-        assert p.lds_bytes == 16 * s * 16 * (16 * rw + blk // 4 * cw)
-        assert p.mf_block == blk
+        assert p.lds_bytes == 16 * s * j * (16 * rw + blk // 4 * cw)
+        assert p.mf_block == blk and p.slab_rows == j
 
 
 def test_mfma_block_zero_means_32():
     p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 2, 4, 4, 2, 0, 0, 0), 8, 64, 64)
-    assert p.mf_block == 32 and p.grid == 8
+    assert p.mf_block == 32 and p.slab_rows == 16 and p.grid == 8
 
 
 def test_mfma_direct_to_lds_fallback_instances_exist():
     """A direct-to-LDS plan whose launch finds unaligned x or d_dv rows runs the same work items through the register
-    ring with 4 stages, 2 register slabs and 4 loader wavefronts of 32-column wavefronts (half as many column
-    wavefronts for a 16-column plan): that instance exists for every direct-to-LDS one."""
-    for rw, cw, s, rs, lw, de, blk in MFMA_INSTANCES:
+    ring with 4 stages of 16 rows, 2 register slabs and 4 loader wavefronts of 32-column wavefronts (half as many
+    column wavefronts for a 16-column plan): that instance exists for every direct-to-LDS one."""
+    for rw, cw, s, rs, lw, de, blk, j in MFMA_INSTANCES:
         if rs == 0:
             fcw = cw // 2 if blk == 16 else cw
-            assert (rw, fcw, 4, 2, 4, de, 32) in MFMA_INSTANCES
+            assert (rw, fcw, 4, 2, 4, de, 32, 16) in MFMA_INSTANCES
             g.sdm_gx_plan_complete(g.make_mfma_plan(rw, fcw, 4, 2, 4, 0, de), 4, 64, 64)
 
 
@@ -236,9 +239,11 @@ def test_mfma_direct_to_lds_rejects_missing_instances():
     for s, rs, lw in ((8, 0, 1), (4, 0, 2), (2, 0, 1), (8, 2, 4)):
         with pytest.raises(ValueError):
             g.sdm_gx_plan_complete(g.make_mfma_plan(2, 4, s, rs, lw), 4, 128, 128)
-    for rw, cw, s, rs, lw, blk in ((1, 1, 4, 0, 1, 16), (1, 2, 4, 4, 2, 16), (1, 2, 4, 0, 1, 8), (1, 2, 4, 0, 1, 64)):
+    for rw, cw, s, rs, lw, blk, j in ((1, 1, 4, 0, 1, 16, 0), (1, 2, 4, 4, 2, 16, 0), (1, 2, 4, 0, 1, 8, 0),
+                                      (1, 2, 4, 0, 1, 64, 0), (1, 2, 4, 0, 1, 32, 32), (1, 2, 8, 0, 2, 16, 32),
+                                      (1, 2, 4, 4, 2, 32, 32), (1, 2, 4, 0, 1, 16, 24)):
         with pytest.raises(ValueError):
-            g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, 0, 0, blk), 4, 64, 64)
+            g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, 0, 0, blk, j), 4, 64, 64)
 
 def test_plan_complete_rows_beyond_c():
     with pytest.raises(ValueError):

@@ -104,11 +104,12 @@ def all_plans(C, hd=64):
                             yield plan
     for rw in (1, 2):
         for cw in (1, 2, 4, 8):
-            for stages, rs, lw, blk in ((4, 2, 2, 32), (4, 2, 4, 32), (4, 4, 2, 32), (4, 4, 4, 32), (4, 0, 1, 32),
-                                        (8, 0, 2, 32), (4, 0, 1, 16), (8, 0, 2, 16)):
+            for stages, rs, lw, blk, j in ((4, 2, 2, 32, 16), (4, 2, 4, 32, 16), (4, 4, 2, 32, 16), (4, 4, 4, 32, 16),
+                                           (4, 0, 1, 32, 16), (8, 0, 2, 32, 16), (4, 0, 1, 16, 16), (8, 0, 2, 16, 16),
+                                           (4, 0, 1, 16, 32)):
                 for de in (0, 1):
                     for wgs in (0, 2):
-                        plan = g.make_mfma_plan(rw, cw, stages, rs, lw, wgs, de, blk)
+                        plan = g.make_mfma_plan(rw, cw, stages, rs, lw, wgs, de, blk, j)
                         try:
                             g.sdm_gx_plan_complete(plan, 1, C, hd)
                         except ValueError:
@@ -121,8 +122,8 @@ def dma_plans():
     return [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0) for rw, cw in ((1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2),
                                                                       (2, 4)) for s, lw, wgs in ((4, 1, 3), (8, 2, 0))] \
         + [g.make_mfma_plan(2, 4, 4, 0, 1, 5, 1)] \
-        + [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0, 16) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-           for s, lw, wgs in ((4, 1, 3), (8, 2, 0))]
+        + [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
+           for s, lw, wgs, j in ((4, 1, 3, 16), (8, 2, 0, 16), (4, 1, 2, 32))]
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8),
@@ -336,7 +337,7 @@ def test_no_kernel_instance_spills():
     for plan in all_plans(256, 4096):
         if plan.engine == g.SDM_GX_ENGINE_MFMA:
             key = ("mfma", plan.mf_row_waves, plan.mf_col_waves, plan.mf_stages, plan.mf_reg_slabs,
-                   plan.mf_loader_waves, plan.mf_du_at_end, plan.mf_block)
+                   plan.mf_loader_waves, plan.mf_du_at_end, plan.mf_block, plan.slab_rows)
             waves = plan.mf_row_waves * plan.mf_col_waves + plan.mf_loader_waves
         else:
             key = ("valu", plan.rows_per_wave, plan.cols_per_lane, plan.waves_per_wg, plan.staging)
@@ -347,7 +348,7 @@ def test_no_kernel_instance_spills():
         attrs = g.sdm_gx_kernel_attrs(plan)
         assert attrs["scratch_bytes"] == 0, (key, attrs)
         assert attrs["vgprs"] * -(-waves // 4) <= 512, (key, attrs)
-    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 53
+    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 58
 
 
 def test_kernel_attrs_report_no_scratch():

@@ -206,6 +206,31 @@ def test_mfma_direct_to_lds_plans(C, hd, ld, res):
             assert_matches(got, want, du, hd, f"direct-to-LDS plan {plan} mode {mode}")
 
 
+@pytest.mark.parametrize("C,ld,plan", [
+    (1, None, None), (3, None, None),
+    (32, 1 << 20, ("mfma", 1, 4, 4, 0, 1, 0, 0, 16, 16)),     # direct-to-LDS (rows 16-byte aligned)
+    (32, None, ("mfma", 1, 4, 4, 0, 1, 0, 0, 16, 32)),        # ld = hd = 2^20 - 1: runs through the register ring
+    (33, None, ("valu", 4, 4, 8, 0)),
+])
+def test_widest_hd(C, ld, plan):
+    """hd = 2^20 - 1, the largest row the checks accept, on both engines; the oracle runs on a sample of columns
+    (each output column's chain reads only that column of d_dv), including the last ones."""
+    N, P, hd = 2, 1, (1 << 20) - 1
+    ld = ld or hd
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "normal", seed=C + ld)
+    case = DeviceCase(x, dv, du, hd)
+    if plan is not None:
+        plan = g.make_mfma_plan(*plan[1:]) if plan[0] == "mfma" else g.make_plan(*plan[1:])
+    say(f"widest hd C={C} ld={ld} plan {plan}")
+    got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, plan)
+    rng = np.random.default_rng(C)
+    cols = np.unique(np.concatenate([rng.integers(0, hd, 1500), np.arange(hd - 70, hd), np.arange(0, 70)]))
+    want = expected(x, np.ascontiguousarray(dv[:, :, cols]), np.ascontiguousarray(du[:, :, cols]), len(cols), 0, N)
+    assert_matches(np.ascontiguousarray(got[:, :, cols]), want, du[:, :, cols], len(cols), f"widest hd C={C}")
+    if ld > hd:
+        assert (got.view(np.uint32)[:, :, hd:] == du.view(np.uint32)[:, :, hd:]).all(), "padding column written"
+
+
 def test_mfma_engine_many_items_per_workgroup():
     """Persistent matrix-core workgroups walking long ranges of work items (chunks x row groups x column groups),
     ragged in rows and columns, per step and fused."""

@@ -128,7 +128,7 @@ constexpr int kDefaultCus = 256;                // MI355X
 const sdm_gx::MfmaEntry* find_mfma(const sdm_gx_plan_t& p) {
     return sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages, p.mf_reg_slabs, p.mf_loader_waves,
                                     p.mf_du_at_end, p.mf_block > 0 ? p.mf_block : 32,
-                                    p.slab_rows > 0 ? p.slab_rows : 16);
+                                    p.slab_rows > 0 ? p.slab_rows : 16, 0);
 }
 
 // Geometry of the matrix-core engine for nchunks chunks: work items and the persistent grid.
@@ -214,25 +214,43 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 // allow_mfma = false forces the vector-ALU engine (row strides too large for the matrix-core engine's 32-bit
 // buffer offsets).
 int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out,
-             bool allow_mfma = true) {
+             bool allow_mfma, bool dma_ok) {
     if (!out) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
     if (num_cus < 1) num_cus = kDefaultCus;
-    if (allow_mfma && C >= 32 && hd <= 128) {
+    if (allow_mfma && C >= 32 && (dma_ok || hd <= 128)) {
         sdm_gx_plan_t p{};
         p.engine = SDM_GX_ENGINE_MFMA;
-        p.mf_block = 16;
-        p.mf_row_waves = C > 64 ? 2 : 1;
-        p.mf_col_waves = hd > 32 ? 4 : 2;
-        if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
-        p.mf_stages = 4;
-        p.mf_reg_slabs = 0;
-        p.mf_loader_waves = 1;
-        p.mf_workgroups = (p.mf_row_waves * p.mf_col_waves < 8 ? 2 : 1) * num_cus;
-        p.slab_rows = 16;
-        int st = complete_plan(&p, nchunks, C, hd, lds_limit);
-        if (st == SDM_GX_OK && p.grid <= num_cus) {             // one workgroup per CU: 32-row stages
-            p.slab_rows = 32;
+        int st;
+        if (dma_ok) {                                   // direct-to-LDS slabs, 16-column wavefronts
+            p.mf_block = 16;
+            p.mf_row_waves = C > 64 ? 2 : 1;
+            p.mf_col_waves = hd > 32 ? 4 : 2;
+            if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
+            p.mf_stages = 4;
+            p.mf_reg_slabs = 0;
+            p.mf_loader_waves = 1;
+            const int64_t items = nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves);
+            p.mf_workgroups = (p.mf_row_waves * p.mf_col_waves < 8 && items < 4 * num_cus ? 2 : 1) * num_cus;
+            p.slab_rows = 16;
+            st = complete_plan(&p, nchunks, C, hd, lds_limit);
+            if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU: 32-row stages
+                p.slab_rows = 32;
+                st = complete_plan(&p, nchunks, C, hd, lds_limit);
+            }
+        } else {                                        // register ring, 32-column wavefronts
+            p.mf_block = 32;
+            p.mf_row_waves = C > 64 ? 2 : 1;
+            p.mf_col_waves = static_cast<int32_t>(cdiv(hd, 32) > 2 ? 4 : cdiv(hd, 32));
+            p.mf_stages = 4;
+            p.mf_reg_slabs = 4;
+            p.mf_loader_waves = p.mf_row_waves * p.mf_col_waves <= 2 ? 2 : 4;
+            p.mf_workgroups = num_cus;
+            if (p.mf_row_waves == 2 && p.mf_col_waves == 4) {   // 128 x 128 items: two workgroups per CU
+                p.mf_reg_slabs = 2;
+                p.mf_du_at_end = 1;
+                p.mf_workgroups = 2 * num_cus;
+            }
             st = complete_plan(&p, nchunks, C, hd, lds_limit);
         }
         if (st == SDM_GX_OK) {
@@ -279,11 +297,14 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
 // The matrix-core engine addresses a chunk of d_u with 32-bit byte offsets.
 bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1) << 31); }
 
-// Direct-to-LDS slabs (mf_reg_slabs 0) move 16-byte groups and address a chunk of d_dv with 32-bit byte offsets:
-// x and d_dv rows must start on 16-byte boundaries.
-bool dma_layout_ok(const float* x, const float* dv, int64_t C, int64_t ld_dv) {
-    return reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0 && C % 4 == 0 &&
-           ld_dv % 4 == 0 && C * ld_dv * 4 < (int64_t(1) << 31);
+// Direct-to-LDS slabs (mf_reg_slabs 0) move 16-byte groups, all rows of x and of d_dv at one offset from a 16-byte
+// boundary (C and ld_dv multiples of 4), and address a chunk of d_dv, and the rows past C that pad its last slab,
+// with 32-bit byte offsets.
+bool dma_strides_ok(int64_t C, int64_t ld_dv) {
+    return C % 4 == 0 && ld_dv % 4 == 0 && (C + 32) * ld_dv * 4 < (int64_t(1) << 31);
+}
+bool rows_aligned16(const float* x, const float* dv) {
+    return reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0;
 }
 
 // ---- launching ----------------------------------------------------------------------------------------------------
@@ -312,17 +333,25 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
         if (!e) return SDM_GX_ERR_PLAN;
         if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
         sdm_gx_plan_t q = p;
-        if (e->reg_slabs == 0 && !dma_layout_ok(x, dv, C, ld_dv)) {
-            // slabs cannot go straight to LDS: the same work items through the register ring (32-column
-            // wavefronts: a mf_block 16 tile of 2k column wavefronts is k of them)
-            if (e->block == 16) q.mf_col_waves = e->col_waves / 2;
-            q.mf_block = 32;
-            q.slab_rows = 16;
-            q.mf_stages = 4;
-            q.mf_reg_slabs = 2;
-            q.mf_loader_waves = 4;
-            e = find_mfma(q);
-            if (!e) return SDM_GX_ERR_PLAN;
+        if (e->reg_slabs == 0) {
+            const sdm_gx::MfmaEntry* twin = nullptr;
+            if (dma_strides_ok(C, ld_dv) && !rows_aligned16(x, dv))      // rows off a 16-byte boundary
+                twin = sdm_gx::find_mfma_kernel(e->row_waves, e->col_waves, e->stages, 0, e->loader_waves,
+                                                e->du_at_end, e->block, e->slab_rows, 1);
+            if (twin) {
+                e = twin;
+            } else if (!dma_strides_ok(C, ld_dv) || !rows_aligned16(x, dv)) {
+                // slabs cannot go straight to LDS: the same work items through the register ring (32-column
+                // wavefronts: a mf_block 16 tile of 2k column wavefronts is k of them)
+                if (e->block == 16) q.mf_col_waves = e->col_waves / 2;
+                q.mf_block = 32;
+                q.slab_rows = 16;
+                q.mf_stages = 4;
+                q.mf_reg_slabs = 2;
+                q.mf_loader_waves = 4;
+                e = find_mfma(q);
+                if (!e) return SDM_GX_ERR_PLAN;
+            }
         }
         const MfmaGeom g = mfma_geom(q, nchunks, C, hd);
         if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
@@ -390,7 +419,7 @@ int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* 
 }
 
 // Plan (given or planned) for nchunks chunks on a device with `info`; ld_u: the row stride the launch will use.
-int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u,
+int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv,
                  const DeviceInfo& info, sdm_gx_plan_t* out) {
     if (given) {
         *out = *given;
@@ -400,7 +429,8 @@ int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t
         if (out->engine == SDM_GX_ENGINE_MFMA && !mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
         return SDM_GX_OK;
     }
-    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, mfma_strides_ok(C, ld_u));
+    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, mfma_strides_ok(C, ld_u),
+                    dma_strides_ok(C, ld_dv));
 }
 
 int check_device_pointers(const float* du, const float* x, const float* dv, int dev) {
@@ -428,7 +458,7 @@ int sdm_gx_gemm_ex(float* d_u, int64_t ld_u, const float* x, const float* d_dv, 
     if ((st = current_device(&dev, &info))) return st;
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_plan_t p;
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &p))) return st;
     return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, static_cast<hipStream_t>(stream));
 }
 
@@ -458,10 +488,10 @@ int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_d
     sdm_gx_plan_t p;
     if (mode == SDM_GX_STEPS_FUSED) {
         const int64_t nchunks = (ti_end - ti_begin) * P;
-        if ((st = resolve_plan(plan, nchunks, C, hd, ld_u, info, &p))) return st;
+        if ((st = resolve_plan(plan, nchunks, C, hd, ld_u, ld_dv, info, &p))) return st;
         return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti_begin * P, nchunks, C, hd, s);
     }
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &p))) return st;
     for (int64_t k = 0; k < ti_end - ti_begin; ++k) {
         const int64_t ti = mode == SDM_GX_STEPS_FORWARD ? ti_begin + k : ti_end - 1 - k;
         if ((st = launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, s))) return st;
@@ -480,7 +510,7 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
     int st = device_info(dev, &info);
     if (st) return st;
     if (!info.gfx950) return SDM_GX_ERR_DEVICE;
-    if ((st = plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out))) return st;
+    if ((st = plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, true, dma_strides_ok(C, hd)))) return st;
     const void* fn;
     int threads, dyn_lds;
     if (out->engine == SDM_GX_ENGINE_MFMA) {
@@ -503,7 +533,7 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
 
 int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int32_t num_cus, int32_t lds_per_cu,
                     sdm_gx_plan_t* out) {
-    return plan_for(nchunks, C, hd, num_cus, lds_per_cu, out);
+    return plan_for(nchunks, C, hd, num_cus, lds_per_cu, out, true, dma_strides_ok(C, hd));
 }
 
 int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd, int32_t lds_per_cu) {
@@ -524,8 +554,8 @@ int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* 
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_launch_t l;
     std::memset(&l, 0, sizeof(l));
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, info, &l.plan_step))) return st;
-    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, ld_u, info, &l.plan_fused))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &l.plan_step))) return st;
+    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, ld_u, ld_dv, info, &l.plan_fused))) return st;
     l.device = dev;
     l.d_u = d_u;
     l.x = x;

@@ -30,11 +30,12 @@ struct MfmaEntry {
     int lds_bytes;      // static LDS of the instance
     int block;          // MFMA block: 32 (64x32 tile per compute wavefront) or 16 (64x16)
     int slab_rows;      // chain rows per LDS stage (16, or 32 in some direct-to-LDS instances)
+    int aln;            // direct-to-LDS only: 1 = for x and d_dv rows that start off a 16-byte boundary
 };
 
 // The kernel instance for the given shape parameters, or nullptr. Launched with a
 // 64 * (row_waves * col_waves + loader_waves) thread block and one MfmaArgs argument passed by value.
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
-                                  int du_at_end, int block, int slab_rows);
+                                  int du_at_end, int block, int slab_rows, int aln);
 
 }  // namespace sdm_gx

@@ -358,19 +358,24 @@ template <> struct MfShape<16> {
     __device__ static __forceinline__ int lane_row(int lane) { return 4 * (lane >> 4); }
 };
 
-template <int RW, int QW, int S, int LW, int DU_AT_END, int MINW, int MS, int J>
+template <int RW, int QW, int S, int LW, int DU_AT_END, int MINW, int MS, int J, int ALN>
 __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(const MfmaArgs a) {
     typedef MfShape<MS> M;
     typedef typename M::acc_t acc_t;
     constexpr int NR = M::NR;
     constexpr int CWV = RW * QW;
     constexpr int XW = 64 * RW, DW = MS * QW;          // x / d_dv columns of a work item
-    constexpr int GX = XW / 4, GD = DW / 4, GS = J * (GX + GD);   // float4 groups of one slab
-    constexpr int NI = GS / 64, NIX = J * GX / 64;      // DMA instructions per slab, of which x
+    // LDS rows: ALN = 1 (rows start 4, 8 or 12 bytes past a 16-byte boundary) loads each row from the boundary below
+    // its start, one more 16-byte group per row; the first `shift` floats of an LDS row are then not the row's.
+    constexpr int XR = XW + 4 * ALN, DR = DW + 4 * ALN;          // LDS row widths in floats
+    constexpr int GXR = XR / 4, GDR = DR / 4;                    // 16-byte groups per LDS row
+    constexpr int NIX = (J * GXR + 63) / 64, NID = (J * GDR + 63) / 64;   // DMA instructions per slab: x, d_dv
+    constexpr int NI = NIX + NID, GS = NI * 64;         // float4 groups of one stage (with padding lanes)
     constexpr int PERW = NI / LW;                       // per loader wavefront per slab
     constexpr int K = kOperandGroup;
+    constexpr int kNoSource = 0x3FFFFFF0;               // padding lanes: a float offset past every buffer range
     static_assert((S & (S - 1)) == 0 && S >= 2, "S: power of two");
-    static_assert(NIX % LW == 0 && (NI - NIX) % LW == 0, "loader wavefronts split x and d_dv evenly");
+    static_assert(NIX % LW == 0 && NID % LW == 0, "loader wavefronts split x and d_dv evenly");
     static_assert((S - 2) * PERW <= 63, "slabs in flight exceed the vmcnt range");
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -394,20 +399,24 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
         for (int k = 0; k < PERW; ++k) {
             const int m = wl + k * LW;
             if (k < NIX / LW) {
-                const int g = m * 64 + lane, jj = g / GX;
-                off[k] = jj * C + (g - jj * GX) * 4;
+                const int g = m * 64 + lane, jj = g / GXR;
+                off[k] = g < J * GXR ? jj * C + (g - jj * GXR) * 4 : kNoSource;
             } else {
-                const int h = (m - NIX) * 64 + lane, jj = h / GD;
-                off[k] = jj * static_cast<int>(a.ld_dv) + (h - jj * GD) * 4;
+                const int h = (m - NIX) * 64 + lane, jj = h / GDR;
+                off[k] = h < J * GDR ? jj * static_cast<int>(a.ld_dv) + (h - jj * GDR) * 4 : kNoSource;
             }
         }
+        // floats from the 16-byte boundary below each row start (the same for every row: C and ld_dv are
+        // multiples of 4); that boundary is in the same 16-byte block, hence the same page, as the row start
+        const int sx = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
+        const int sd = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
         ChunkCursor lc;
         lc.init(first, nch, a.ncg);
         int ls = 0;
         auto issue = [&](int stage) {                   // slab ls of item lc into `stage`
             const int64_t n = a.n_begin + lc.n;
-            const int xo = ls * J * C + lc.rg * XW;                      // first float of the slab in x's chunk
-            const int64_t dvo = static_cast<int64_t>(ls * J) * a.ld_dv + lc.cg * DW;
+            const int xo = ls * J * C + lc.rg * XW - sx;                 // first float of the slab in x's chunk
+            const int64_t dvo = static_cast<int64_t>(ls * J) * a.ld_dv + lc.cg * DW - sd;
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float*>(a.x) + n * C * C + xo, (short)0, (C * C - xo) * 4, kBufferFlags);
             const int dv_end = static_cast<int>((static_cast<int64_t>(C - 1) * a.ld_dv + hd - dvo) * 4);
@@ -418,9 +427,9 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
             for (int k = 0; k < PERW; ++k) {
                 float* dst = st + (wl + k * LW) * 256;
                 if (k < NIX / LW)
-                    load_lds16(xr, dst, off[k] * 4);
+                    load_lds16(xr, dst, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
                 else
-                    load_lds16(dr, dst, off[k] * 4);
+                    load_lds16(dr, dst, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
             }
             if (++ls == ns) {
                 ls = 0;
@@ -438,17 +447,19 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
         }
     } else {
         const int rw = wave / QW, qw = wave - (wave / QW) * QW;
-        const float* xs0 = reinterpret_cast<const float*>(&ring[0][0]) + rw * 64 + lane;
-        const float* ds0 = reinterpret_cast<const float*>(&ring[0][0]) + J * XW + qw * MS + (lane & (MS - 1));
+        const int sx = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
+        const int sd = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
+        const float* xs0 = reinterpret_cast<const float*>(&ring[0][0]) + rw * 64 + lane + sx;
+        const float* ds0 = reinterpret_cast<const float*>(&ring[0][0]) + NIX * 256 + qw * MS + (lane & (MS - 1)) + sd;
         constexpr int STAGE_FLOATS = GS * 4;
         acc_t acc;
-        auto compute = [&](const float* xs, const float* ds) {   // 16 chain steps from one ring stage
+        auto compute = [&](const float* xs, const float* ds) {   // J chain steps from one ring stage
             float ra[2][K], rb[2][K];
             auto rd = [&](int buf, int grp) {
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
-                    ra[buf][k] = xs[(grp * K + k) * XW];
-                    rb[buf][k] = ds[(grp * K + k) * DW];
+                    ra[buf][k] = xs[(grp * K + k) * XR];
+                    rb[buf][k] = ds[(grp * K + k) * DR];
                 }
             };
             rd(0, 0);
@@ -462,8 +473,8 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        auto compute_tail = [&](const float* xs, const float* ds, int nk) {   // the first nk < 16 chain steps
-            for (int k = 0; k < nk; ++k) acc = M::step(xs[k * XW], ds[k * DW], acc);
+        auto compute_tail = [&](const float* xs, const float* ds, int nk) {   // the first nk < J chain steps
+            for (int k = 0; k < nk; ++k) acc = M::step(xs[k * XR], ds[k * DR], acc);
         };
         ChunkCursor cc;
         cc.init(first, nch, a.ncg);
@@ -525,19 +536,23 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 // wavefronts and 4 register slabs. Two instances read d_u at the item's end and are built for two workgroups per CU.
 #define SDM_GX_MF_X(RW, QW, S, R, LW, DE, MW) \
     {RW, QW, S, R, LW, DE, reinterpret_cast<const void*>(&gx_mfma_kernel<RW, QW, S, R, LW, DE, MW>), \
-     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW)), 32, kSlabRows},
+     static_cast<int>(sizeof(f32x4a) * S * kSlabRows * (16 * RW + 8 * QW)), 32, kSlabRows, 0},
 #define SDM_GX_MF(RW, QW, S, R, LW) SDM_GX_MF_X(RW, QW, S, R, LW, 0, 1)
 #define SDM_GX_MF_RL(RW, QW) SDM_GX_MF(RW, QW, 4, 4, 4) SDM_GX_MF(RW, QW, 4, 2, 4) SDM_GX_MF(RW, QW, 4, 4, 2) \
     SDM_GX_MF(RW, QW, 4, 2, 2)
 
 // Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages of 16 chain rows and 1 loader wavefront, and
 // with S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
-// workgroups per CU; the 16-column tiles also with 32-row stages (4 stages, 1 loader wavefront).
-#define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) \
-    {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J>), \
-     static_cast<int>(sizeof(f32x4a) * S * J * (16 * RW + MS / 4 * QW)), MS, J},
+// workgroups per CU; the 16-column tiles also with 32-row stages (4 stages, 1 loader wavefront), and with 4 stages
+// and 1 loader wavefront for rows off a 16-byte boundary (ALN = 1; chosen at launch from the pointers).
+#define SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, ALN) \
+    {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J, ALN>), \
+     static_cast<int>(sizeof(f32x4a) * S * 64 * \
+                      ((J * (16 * RW + ALN) + 63) / 64 + (J * (MS / 4 * QW + ALN) + 63) / 64)), MS, J, ALN},
+#define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, 0)
 #define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS, 16)
-#define SDM_GX_MD3(RW, QW) SDM_GX_MD2(RW, QW, 16) SDM_GX_MD(RW, QW, 4, 1, 0, 1, 16, 32)
+#define SDM_GX_MD3(RW, QW) SDM_GX_MD2(RW, QW, 16) SDM_GX_MD(RW, QW, 4, 1, 0, 1, 16, 32) \
+    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 1) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 1)
 
 const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)
@@ -553,11 +568,11 @@ const MfmaEntry kMfmaTable[] = {
 }  // namespace
 
 const MfmaEntry* find_mfma_kernel(int row_waves, int col_waves, int stages, int reg_slabs, int loader_waves,
-                                  int du_at_end, int block, int slab_rows) {
+                                  int du_at_end, int block, int slab_rows, int aln) {
     for (const MfmaEntry& e : kMfmaTable)
         if (e.row_waves == row_waves && e.col_waves == col_waves && e.stages == stages && e.reg_slabs == reg_slabs &&
             e.loader_waves == loader_waves && e.du_at_end == du_at_end && e.block == block &&
-            e.slab_rows == slab_rows)
+            e.slab_rows == slab_rows && e.aln == aln)
             return &e;
     return nullptr;
 }

@@ -135,28 +135,48 @@ def mfma_grid(items, workgroups=256):
     return cdiv(items, per)
 
 
+def dma_ok(C, ld):
+    return C % 4 == 0 and ld % 4 == 0 and (C + 32) * ld * 4 < 2 ** 31
+
+
 def test_plan_for_emits_supported_plans():
     shapes = [(C, hd) for C in (1, 2, 3, 4, 5, 16, 17, 31, 32, 64, 100, 128, 200, 256)
               for hd in (1, 3, 4, 63, 64, 65, 100, 128, 129, 200, 256, 257, 1000, 4100)]
     for nchunks in (0, 1, 7, 128, 4096):
         for C, hd in shapes:
             p = g.sdm_gx_plan_for(nchunks, C, hd)
-            # engine rule: matrix cores for 32 <= C and hd <= 128
-            assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and hd <= 128 else g.SDM_GX_ENGINE_VALU)
-            if p.engine == g.SDM_GX_ENGINE_MFMA:
+            # engine rule: matrix cores for 32 <= C when slabs can go straight to LDS (C and the row stride, taken
+            # as hd here, multiples of 4), or for hd <= 128 through the register ring
+            assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and (dma_ok(C, hd) or hd <= 128)
+                                else g.SDM_GX_ENGINE_VALU)
+            if p.engine == g.SDM_GX_ENGINE_MFMA and dma_ok(C, hd):
                 # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 columns (32 when hd <= 32
-                # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU, 32-row stages when
-                # each CU holds one workgroup
+                # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU unless the items are
+                # many (4 or more per CU), 32-row stages when each CU holds one workgroup
                 assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 4 and p.mf_loader_waves == 1
                 assert p.mf_row_waves == (2 if C > 64 else 1)
                 wide = hd > 32 and nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) >= 256
                 assert p.mf_col_waves == (4 if wide else 2)
                 assert p.mf_du_at_end == 0
-                assert p.mf_workgroups == (512 if p.mf_row_waves * p.mf_col_waves < 8 else 256)
                 items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves)
+                two = p.mf_row_waves * p.mf_col_waves < 8 and items < 4 * 256
+                assert p.mf_workgroups == (512 if two else 256)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
                 assert p.slab_rows == (32 if p.grid <= 256 else 16)
                 assert p.lds_bytes == 16 * 4 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
+                continue
+            if p.engine == g.SDM_GX_ENGINE_MFMA:
+                # register ring, 32-column wavefronts, one work item per chunk up to 128 x 128
+                assert p.mf_block == 32 and p.mf_stages == 4
+                assert p.mf_row_waves == (2 if C > 64 else 1)
+                assert p.mf_col_waves == (4 if cdiv(hd, 32) > 2 else cdiv(hd, 32))
+                big = (p.mf_row_waves, p.mf_col_waves) == (2, 4)      # 128 x 128 items: two workgroups per CU
+                assert p.mf_reg_slabs == (2 if big else 4)
+                assert p.mf_du_at_end == (1 if big else 0) and p.mf_workgroups == (512 if big else 256)
+                assert p.mf_loader_waves == (2 if p.mf_row_waves * p.mf_col_waves <= 2 else 4)
+                items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 32 * p.mf_col_waves)
+                assert p.grid == mfma_grid(items, p.mf_workgroups)
+                assert p.lds_bytes == 16 * 4 * 16 * (16 * p.mf_row_waves + 8 * p.mf_col_waves)
                 continue
             assert p.rows_per_wave in (1, 2, 4, 8, 16) and p.rows_per_wave <= C
             assert p.cols_per_lane in (1, 2, 4) and p.rows_per_wave * p.cols_per_lane <= 64
@@ -207,6 +227,7 @@ MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs
                  [(2, 4, 4, 0, 1, 1, 32, 16)] + \
                  [(rw, cw, s, 0, lw, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
                   for s, lw, j in ((4, 1, 16), (8, 2, 16), (4, 1, 32))]
+# and, for each 16-column (4 stages, 1 loader) instance, a twin for rows off a 16-byte boundary, picked at launch
 
 
 @pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk,j", MFMA_INSTANCES)

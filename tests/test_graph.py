@@ -15,7 +15,8 @@ SHAPES = [  # N, P, C, hd, ld, residues, engine expected from the planner
     (16, 4, 64, 64, 64, (0, 0, 0), g.SDM_GX_ENGINE_MFMA),
     (12, 3, 100, 96, 99, (4, 8, 12), g.SDM_GX_ENGINE_MFMA),
     (8, 2, 16, 40, 41, (8, 4, 0), g.SDM_GX_ENGINE_VALU),
-    (6, 2, 64, 256, 260, (4, 0, 4), g.SDM_GX_ENGINE_VALU),
+    (6, 2, 64, 256, 260, (4, 0, 4), g.SDM_GX_ENGINE_MFMA),      # rows 4 bytes past a 16-byte boundary
+    (6, 2, 64, 200, 201, (4, 0, 4), g.SDM_GX_ENGINE_VALU),
 ]
 
 

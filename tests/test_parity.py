@@ -189,11 +189,15 @@ def test_mfma_engine_single_rounding():
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(148, 70, 76, (0, 0, 0)), (64, 64, 64, (0, 0, 0)), (128, 128, 128, (4, 0, 0)),
-                                        (36, 100, 104, (0, 0, 0)), (64, 128, 131, (0, 4, 0)), (148, 70, 76, (0, 0, 8))])
+                                        (36, 100, 104, (0, 0, 0)), (64, 128, 131, (0, 4, 0)), (148, 70, 76, (0, 0, 8)),
+                                        (64, 256, 260, (4, 4, 0)), (64, 64, 68, (0, 12, 4)), (36, 100, 104, (8, 4, 12)),
+                                        (100, 33, 36, (0, 8, 0)), (128, 40, 44, (12, 0, 4))])
 def test_mfma_direct_to_lds_plans(C, hd, ld, res):
     """Slabs moved straight from memory into LDS (mf_reg_slabs 0): ragged rows, columns and last slabs (C % 16 != 0
-    runs only the chain's own steps), several items per workgroup, per step and fused. Where x or d_dv rows are not
-    16-byte aligned (d_dv at +4 B, ld 131, x at +8 B) the launch takes the register ring, with the same bits."""
+    runs only the chain's own steps), several items per workgroup, per step and fused. Rows that start 4, 8 or 12
+    bytes past a 16-byte boundary (x or d_dv base off, C and ld multiples of 4) load from the boundary below and
+    skip the first floats of each LDS row (the unaligned-row instances); with ld 131 the rows cannot share one offset
+    and the launch takes the register ring. Same bits in every case."""
     N, P = 12, 4
     x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C * 3 + hd)
     case = DeviceCase(x, dv, du, hd, res_u=res[0], res_v=res[1], res_x=res[2])
@@ -373,7 +377,7 @@ def test_no_kernel_instance_spills():
         attrs = g.sdm_gx_kernel_attrs(plan)
         assert attrs["scratch_bytes"] == 0, (key, attrs)
         assert attrs["vgprs"] * -(-waves // 4) <= 512, (key, attrs)
-    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 58
+    assert len([k for k in seen if k[0] == "valu"]) > 100 and len([k for k in seen if k[0] == "mfma"]) == 58    # the 10 unaligned-row twins are not plan-selectable
 
 
 def test_kernel_attrs_report_no_scratch():

@@ -337,7 +337,8 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
             const sdm_gx::MfmaEntry* twin = nullptr;
             if (dma_strides_ok(C, ld_dv) && !rows_aligned16(x, dv))      // rows off a 16-byte boundary
                 twin = sdm_gx::find_mfma_kernel(e->row_waves, e->col_waves, e->stages, 0, e->loader_waves,
-                                                e->du_at_end, e->block, e->slab_rows, 1);
+                                                e->du_at_end, e->block, e->slab_rows,
+                                                reinterpret_cast<uintptr_t>(x) % 16 == 0 ? 2 : 3);
             if (twin) {
                 e = twin;
             } else if (!dma_strides_ok(C, ld_dv) || !rows_aligned16(x, dv)) {

@@ -30,7 +30,7 @@ struct MfmaEntry {
     int lds_bytes;      // static LDS of the instance
     int block;          // MFMA block: 32 (64x32 tile per compute wavefront) or 16 (64x16)
     int slab_rows;      // chain rows per LDS stage (16, or 32 in some direct-to-LDS instances)
-    int aln;            // direct-to-LDS only: 1 = for x and d_dv rows that start off a 16-byte boundary
+    int aln;            // direct-to-LDS only: for rows that start off a 16-byte boundary, 2: d_dv rows, 3: x too
 };
 
 // The kernel instance for the given shape parameters, or nullptr. Launched with a

@@ -365,9 +365,11 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
     constexpr int NR = M::NR;
     constexpr int CWV = RW * QW;
     constexpr int XW = 64 * RW, DW = MS * QW;          // x / d_dv columns of a work item
-    // LDS rows: ALN = 1 (rows start 4, 8 or 12 bytes past a 16-byte boundary) loads each row from the boundary below
-    // its start, one more 16-byte group per row; the first `shift` floats of an LDS row are then not the row's.
-    constexpr int XR = XW + 4 * ALN, DR = DW + 4 * ALN;          // LDS row widths in floats
+    // LDS rows: for rows that start 4, 8 or 12 bytes past a 16-byte boundary (ALN bit 0: x, bit 1: d_dv) each row
+    // is loaded from the boundary below its start, one more 16-byte group per row; the first `shift` floats of such
+    // an LDS row are then not the row's.
+    constexpr int AX = ALN & 1, AD = (ALN >> 1) & 1;
+    constexpr int XR = XW + 4 * AX, DR = DW + 4 * AD;            // LDS row widths in floats
     constexpr int GXR = XR / 4, GDR = DR / 4;                    // 16-byte groups per LDS row
     constexpr int NIX = (J * GXR + 63) / 64, NID = (J * GDR + 63) / 64;   // DMA instructions per slab: x, d_dv
     constexpr int NI = NIX + NID, GS = NI * 64;         // float4 groups of one stage (with padding lanes)
@@ -408,8 +410,8 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
         }
         // floats from the 16-byte boundary below each row start (the same for every row: C and ld_dv are
         // multiples of 4); that boundary is in the same 16-byte block, hence the same page, as the row start
-        const int sx = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
-        const int sd = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
+        const int sx = AX ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
+        const int sd = AD ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
         ChunkCursor lc;
         lc.init(first, nch, a.ncg);
         int ls = 0;
@@ -447,8 +449,8 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
         }
     } else {
         const int rw = wave / QW, qw = wave - (wave / QW) * QW;
-        const int sx = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
-        const int sd = ALN ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
+        const int sx = AX ? static_cast<int>(reinterpret_cast<uintptr_t>(a.x) >> 2) & 3 : 0;
+        const int sd = AD ? static_cast<int>(reinterpret_cast<uintptr_t>(a.dv) >> 2) & 3 : 0;
         const float* xs0 = reinterpret_cast<const float*>(&ring[0][0]) + rw * 64 + lane + sx;
         const float* ds0 = reinterpret_cast<const float*>(&ring[0][0]) + NIX * 256 + qw * MS + (lane & (MS - 1)) + sd;
         constexpr int STAGE_FLOATS = GS * 4;
@@ -544,15 +546,18 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 // Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages of 16 chain rows and 1 loader wavefront, and
 // with S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
 // workgroups per CU; the 16-column tiles also with 32-row stages (4 stages, 1 loader wavefront), and with 4 stages
-// and 1 loader wavefront for rows off a 16-byte boundary (ALN = 1; chosen at launch from the pointers).
+// and 1 loader wavefront for rows off a 16-byte boundary (ALN 2: d_dv rows only, ALN 3: x rows too; chosen at
+// launch from the pointers).
 #define SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, ALN) \
     {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J, ALN>), \
      static_cast<int>(sizeof(f32x4a) * S * 64 * \
-                      ((J * (16 * RW + ALN) + 63) / 64 + (J * (MS / 4 * QW + ALN) + 63) / 64)), MS, J, ALN},
+                      ((J * (16 * RW + (ALN & 1)) + 63) / 64 + (J * (MS / 4 * QW + (ALN >> 1)) + 63) / 64)), \
+     MS, J, ALN},
 #define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, 0)
 #define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS, 16)
 #define SDM_GX_MD3(RW, QW) SDM_GX_MD2(RW, QW, 16) SDM_GX_MD(RW, QW, 4, 1, 0, 1, 16, 32) \
-    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 1) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 1)
+    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 2) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 2) \
+    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 3) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 3)
 
 const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)

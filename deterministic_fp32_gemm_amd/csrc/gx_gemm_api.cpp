@@ -194,7 +194,8 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 // (64x64, 64x128 and 128x128 chunks); the vector-ALU chain otherwise (narrow C, where 64-row MFMA tiles would be
 // mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
 //  Matrix cores: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the
-//  32-column MFMA) with slabs moved straight to LDS (4 stages, 1 loader wavefront); work items of 64 or 128 rows
+//  32-column MFMA) with slabs moved straight to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages, and
+//  6 or 8 stages are slower); work items of 64 or 128 rows
 //  (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); enough
 //  workgroups for 8 compute wavefronts per compute unit (two per unit for 64x64 items). Stages of 32 chain rows
 //  when each CU holds one workgroup (half the barrier bubbles, which no other workgroup fills), 16 when it holds two
@@ -227,7 +228,7 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             p.mf_row_waves = C > 64 ? 2 : 1;
             p.mf_col_waves = hd > 32 ? 4 : 2;
             if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
-            p.mf_stages = 4;
+            p.mf_stages = 3;
             p.mf_reg_slabs = 0;
             p.mf_loader_waves = 1;
             const int64_t items = nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves);

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_kernel(cons
 // 64 x 16 contiguous bytes of LDS; each lane names its own source). No register ring: up to S - 1 slabs are in
 // flight per workgroup at no register cost, so a compute unit keeps far more bytes in flight than the register ring
 // allows. Needs x and d_dv rows on 16-byte boundaries (checked on the host).
-//   * Slab q of the workgroup's stream goes to stage q % S. Tick q: the loader waits (vmcnt) until slab q has landed,
+//   * Slab q of the workgroup's stream goes to stage q mod S. Tick q: the loader waits (vmcnt) until slab q has landed,
 //     everyone meets at barrier B_q, the compute wavefronts run slab q, and the loader issues slab q + S - 1 into
 //     stage (q - 1) % S, whose reads by the compute wavefronts ended before B_q.
 //   * Out-of-range sources are cut by the buffer bounds (the chunk's extent): nothing outside the chunk is read.
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
     constexpr int PERW = NI / LW;                       // per loader wavefront per slab
     constexpr int K = kOperandGroup;
     constexpr int kNoSource = 0x3FFFFFF0;               // padding lanes: a float offset past every buffer range
-    static_assert((S & (S - 1)) == 0 && S >= 2, "S: power of two");
+    static_assert(S >= 2, "S: at least two stages");
     static_assert(NIX % LW == 0 && NID % LW == 0, "loader wavefronts split x and d_dv evenly");
     static_assert((S - 2) * PERW <= 63, "slabs in flight exceed the vmcnt range");
     const int lane = static_cast<int>(threadIdx.x) & 63;
@@ -441,11 +441,13 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 #pragma unroll
         for (int m = 0; m < S - 1; ++m)
             if (m < total) issue(m);
+        int ist = S - 1;                                // stage of slab q + S - 1: (q + S - 1) mod S
         for (int64_t q = 0; q < total; ++q) {
             const int64_t rest = total - 1 - q;         // slabs after q already issued: min(S - 2, rest)
             wait_slabs<PERW, S - 2>(rest < S - 2 ? static_cast<int>(rest) : S - 2);
             loader_barrier();                           // B_q: slab q is in LDS
-            if (q + S - 1 < total) issue(static_cast<int>((q + S - 1) & (S - 1)));
+            if (q + S - 1 < total) issue(ist);
+            ist = ist + 1 == S ? 0 : ist + 1;
         }
     } else {
         const int rw = wave / QW, qw = wave - (wave / QW) * QW;
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
         cc.init(first, nch, a.ncg);
         const int lr = M::lane_row(lane);
         const int ld4 = static_cast<int>(a.ld_u) * 4;   // < 2^31 / C: checked on the host
-        int64_t q = 0;
+        int cst = 0;                                    // stage of the next slab
         float u[NR];
         for (int t = 0; t < nmine; ++t) {
             const int64_t n = a.n_begin + cc.n;
@@ -507,11 +509,12 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
                 }
             };
             if (!DU_AT_END) uload();
-            for (int s = 0; s < ns; ++s, ++q) {
+            for (int s = 0; s < ns; ++s) {
                 __syncthreads();                        // B_q: slab q is in LDS
-                const int off = static_cast<int>(q & (S - 1)) * STAGE_FLOATS;
+                const int off = cst * STAGE_FLOATS;
                 if (s * J + J <= C) compute(xs0 + off, ds0 + off);
                 else compute_tail(xs0 + off, ds0 + off, C - s * J);
+                cst = cst + 1 == S ? 0 : cst + 1;
             }
             if (DU_AT_END) uload();
             if (full) {
@@ -543,11 +546,11 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 #define SDM_GX_MF_RL(RW, QW) SDM_GX_MF(RW, QW, 4, 4, 4) SDM_GX_MF(RW, QW, 4, 2, 4) SDM_GX_MF(RW, QW, 4, 4, 2) \
     SDM_GX_MF(RW, QW, 4, 2, 2)
 
-// Direct-to-LDS instances (reg_slabs = 0): every tile with S = 4 stages of 16 chain rows and 1 loader wavefront, and
-// with S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
-// workgroups per CU; the 16-column tiles also with 32-row stages (4 stages, 1 loader wavefront), and with 4 stages
-// and 1 loader wavefront for rows off a 16-byte boundary (ALN 2: d_dv rows only, ALN 3: x rows too; chosen at
-// launch from the pointers).
+// Direct-to-LDS instances (reg_slabs = 0). 32-column tiles: S = 4 stages of 16 chain rows and 1 loader wavefront,
+// and S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
+// workgroups per CU. 16-column tiles: S = 3 stages of 16 or 32 chain rows and 1 loader wavefront (also for rows off
+// a 16-byte boundary, ALN 2: d_dv rows only, ALN 3: x rows too, chosen at launch from the pointers), and S = 8 of
+// 16 rows with 2 loader wavefronts.
 #define SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, ALN) \
     {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J, ALN>), \
      static_cast<int>(sizeof(f32x4a) * S * 64 * \
@@ -555,9 +558,10 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
      MS, J, ALN},
 #define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, 0)
 #define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS, 16)
-#define SDM_GX_MD3(RW, QW) SDM_GX_MD2(RW, QW, 16) SDM_GX_MD(RW, QW, 4, 1, 0, 1, 16, 32) \
-    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 2) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 2) \
-    SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 16, 3) SDM_GX_MD_A(RW, QW, 4, 1, 0, 1, 16, 32, 3)
+#define SDM_GX_MD3(RW, QW) SDM_GX_MD(RW, QW, 3, 1, 0, 1, 16, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, 16, 16) \
+    SDM_GX_MD(RW, QW, 3, 1, 0, 1, 16, 32) \
+    SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 16, 2) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 32, 2) \
+    SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 16, 3) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 32, 3)
 
 const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)

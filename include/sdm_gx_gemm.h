@@ -93,12 +93,13 @@ typedef enum sdm_gx_status {
  *   xcd_remap      1: workgroup ids are permuted so that the workgroups of one chunk run on one XCD (one L2)
  *   slab_rows      staging 1: d_dv rows per LDS slab (0: the planner's choice; clamped to C). The MFMA engine reads
  *                  it too: chain rows per LDS stage, 16 (0 means 16) or 32 (direct-to-LDS 16-column tiles with
- *                  4 stages and 1 loader wavefront)
+ *                  3 stages and 1 loader wavefront)
  * SDM_GX_ENGINE_MFMA (persistent workgroups walking (chunk, row group, column group) work items; the other engine
  * ignores these fields):
  *   mf_row_waves     compute wavefronts along the rows of a work item, 64 rows each (1 or 2)
  *   mf_col_waves     compute wavefronts along its columns, mf_block columns each (1, 2, 4, or 8 with mf_row_waves 1)
- *   mf_stages        LDS ring stages of slab_rows chain rows of x and d_dv (4; 4 or 8 with mf_reg_slabs 0)
+ *   mf_stages        LDS ring stages of slab_rows chain rows of x and d_dv (4 with register slabs; with
+ *                    mf_reg_slabs 0: 4 or 8 for mf_block 32, 3 or 8 for mf_block 16)
  *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4), or 0: the
  *                    loader wavefronts move slabs straight from memory into the LDS ring (buffer loads to LDS), up
  *                    to mf_stages - 1 slabs in flight. That needs x and d_dv rows on 16-byte boundaries (x and d_dv
@@ -110,7 +111,8 @@ typedef enum sdm_gx_status {
  *   mf_workgroups    workgroups to launch (0: one per compute unit); each takes a contiguous range of work items
  *   mf_du_at_end     0: d_u prefetched when a work item starts; 1: read at its end (fewer registers: two workgroups
  *                    fit one compute unit; instances for 128x128 and 64x128 items with 2 register slabs and 4
- *                    loader wavefronts, and for 128x128 items with mf_reg_slabs 0, 4 stages, 1 loader wavefront)
+ *                    loader wavefronts, and for 128x128 items with mf_reg_slabs 0, mf_block 32, 4 stages,
+ *                    1 loader wavefront)
  *   mf_block         the MFMA that runs the chain, by output columns per compute wavefront (0 means 32):
  *                    32: v_mfma_f32_32x32x1_2b_f32, a 64x32 tile per wavefront, 64 cycles per chain step;
  *                    16: v_mfma_f32_16x16x1_4b_f32, a 64x16 tile, 32 cycles per step (half the chain latency of a

@@ -153,7 +153,7 @@ def test_plan_for_emits_supported_plans():
                 # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 columns (32 when hd <= 32
                 # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU unless the items are
                 # many (4 or more per CU), 32-row stages when each CU holds one workgroup
-                assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 4 and p.mf_loader_waves == 1
+                assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1
                 assert p.mf_row_waves == (2 if C > 64 else 1)
                 wide = hd > 32 and nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) >= 256
                 assert p.mf_col_waves == (4 if wide else 2)
@@ -163,7 +163,7 @@ def test_plan_for_emits_supported_plans():
                 assert p.mf_workgroups == (512 if two else 256)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
                 assert p.slab_rows == (32 if p.grid <= 256 else 16)
-                assert p.lds_bytes == 16 * 4 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
+                assert p.lds_bytes == 16 * 3 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
                 continue
             if p.engine == g.SDM_GX_ENGINE_MFMA:
                 # register ring, 32-column wavefronts, one work item per chunk up to 128 x 128
@@ -226,8 +226,8 @@ MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs
                  [(rw, cw, s, 0, lw, 0, 32, 16) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
                  [(2, 4, 4, 0, 1, 1, 32, 16)] + \
                  [(rw, cw, s, 0, lw, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-                  for s, lw, j in ((4, 1, 16), (8, 2, 16), (4, 1, 32))]
-# and, for each 16-column (4 stages, 1 loader) instance, a twin for rows off a 16-byte boundary, picked at launch
+                  for s, lw, j in ((3, 1, 16), (8, 2, 16), (3, 1, 32))]
+# and, for each 16-column (3 stages, 1 loader) instance, twins for rows off a 16-byte boundary, picked at launch
 
 
 @pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk,j", MFMA_INSTANCES)
@@ -260,9 +260,10 @@ def test_mfma_direct_to_lds_rejects_missing_instances():
     for s, rs, lw in ((8, 0, 1), (4, 0, 2), (2, 0, 1), (8, 2, 4)):
         with pytest.raises(ValueError):
             g.sdm_gx_plan_complete(g.make_mfma_plan(2, 4, s, rs, lw), 4, 128, 128)
-    for rw, cw, s, rs, lw, blk, j in ((1, 1, 4, 0, 1, 16, 0), (1, 2, 4, 4, 2, 16, 0), (1, 2, 4, 0, 1, 8, 0),
-                                      (1, 2, 4, 0, 1, 64, 0), (1, 2, 4, 0, 1, 32, 32), (1, 2, 8, 0, 2, 16, 32),
-                                      (1, 2, 4, 4, 2, 32, 32), (1, 2, 4, 0, 1, 16, 24)):
+    for rw, cw, s, rs, lw, blk, j in ((1, 1, 3, 0, 1, 16, 0), (1, 2, 4, 4, 2, 16, 0), (1, 2, 3, 0, 1, 8, 0),
+                                      (1, 2, 3, 0, 1, 64, 0), (1, 2, 4, 0, 1, 32, 32), (1, 2, 8, 0, 2, 16, 32),
+                                      (1, 2, 4, 4, 2, 32, 32), (1, 2, 3, 0, 1, 16, 24), (1, 2, 4, 0, 1, 16, 16),
+                                      (1, 2, 3, 0, 1, 32, 16)):
         with pytest.raises(ValueError):
             g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, 0, 0, blk, j), 4, 64, 64)
 

@@ -105,8 +105,8 @@ def all_plans(C, hd=64):
     for rw in (1, 2):
         for cw in (1, 2, 4, 8):
             for stages, rs, lw, blk, j in ((4, 2, 2, 32, 16), (4, 2, 4, 32, 16), (4, 4, 2, 32, 16), (4, 4, 4, 32, 16),
-                                           (4, 0, 1, 32, 16), (8, 0, 2, 32, 16), (4, 0, 1, 16, 16), (8, 0, 2, 16, 16),
-                                           (4, 0, 1, 16, 32)):
+                                           (4, 0, 1, 32, 16), (8, 0, 2, 32, 16), (3, 0, 1, 16, 16), (8, 0, 2, 16, 16),
+                                           (3, 0, 1, 16, 32)):
                 for de in (0, 1):
                     for wgs in (0, 2):
                         plan = g.make_mfma_plan(rw, cw, stages, rs, lw, wgs, de, blk, j)
@@ -123,7 +123,7 @@ def dma_plans():
                                                                       (2, 4)) for s, lw, wgs in ((4, 1, 3), (8, 2, 0))] \
         + [g.make_mfma_plan(2, 4, 4, 0, 1, 5, 1)] \
         + [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-           for s, lw, wgs, j in ((4, 1, 3, 16), (8, 2, 0, 16), (4, 1, 2, 32))]
+           for s, lw, wgs, j in ((3, 1, 3, 16), (8, 2, 0, 16), (3, 1, 2, 32))]
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8),
@@ -212,8 +212,8 @@ def test_mfma_direct_to_lds_plans(C, hd, ld, res):
 
 @pytest.mark.parametrize("C,ld,plan", [
     (1, None, None), (3, None, None),
-    (32, 1 << 20, ("mfma", 1, 4, 4, 0, 1, 0, 0, 16, 16)),     # direct-to-LDS (rows 16-byte aligned)
-    (32, None, ("mfma", 1, 4, 4, 0, 1, 0, 0, 16, 32)),        # ld = hd = 2^20 - 1: runs through the register ring
+    (32, 1 << 20, ("mfma", 1, 4, 3, 0, 1, 0, 0, 16, 16)),     # direct-to-LDS (rows 16-byte aligned)
+    (32, None, ("mfma", 1, 4, 3, 0, 1, 0, 0, 16, 32)),        # ld = hd = 2^20 - 1: runs through the register ring
     (33, None, ("valu", 4, 4, 8, 0)),
 ])
 def test_widest_hd(C, ld, plan):

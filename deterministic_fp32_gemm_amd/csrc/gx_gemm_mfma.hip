@@ -5,29 +5,34 @@
 //     acc = +0;  acc = fma(x[n, j, i], d_dv[n, j, c], acc) for j = 0..C-1 in order;  d_u[n, i, c] += acc
 // with one separately rounded add.
 //
-// Why the matrix cores can run this chain: an FP32 MFMA with K = 1 (v_mfma_f32_32x32x1_2b_f32) computes, for every
-// element of its 32x32 blocks, d = c + a*b with a single rounding (round to nearest even, subnormals kept): exactly
-// one fmaf step. There is no reduction inside the instruction, so issuing one such MFMA per chain step j, in order,
-// with the accumulator fed back as c, is the chain itself. (Checked bit for bit against fmaf on tens of millions of
-// operand triples, including subnormals, cancellations, signed zeros, Inf and NaN, and by the parity tests.) MFMAs
-// with K > 1 sum several products inside one instruction and are not used.
+// Why the matrix cores can run this chain: an FP32 MFMA with K = 1 (v_mfma_f32_32x32x1_2b_f32,
+// v_mfma_f32_16x16x1_4b_f32) computes, for every element of its blocks, d = c + a*b with a single rounding (round to
+// nearest even, subnormals kept): exactly one fmaf step. There is no reduction inside the instruction, so issuing one
+// such MFMA per chain step j, in order, with the accumulator fed back as c, is the chain itself. (Checked bit for bit
+// against fmaf on tens of millions of operand triples, including subnormals, cancellations, signed zeros, Inf and
+// NaN, and by the parity tests.) MFMAs with K > 1 sum several products inside one instruction and are not used.
 //
-// Structure (one persistent workgroup per compute unit; every global access is in long, coalesced streams):
-//   * Work items are (chunk, row group, column group) tiles of 64*RW rows x 32*QW columns. Each workgroup takes a
-//     contiguous range of items and walks them in order.
-//   * Compute wavefronts (RW x QW of them) each own one 64-row x 32-column output tile: two 32x32 MFMA blocks
-//     stacked along the rows. Lane l supplies A = x[n, j, i0 + l] and B = d_dv[n, j, c0 + l % 32].
-//   * Loader wavefronts (LW of them) stream the x and d_dv rows of all the workgroup's items, 16 chain rows ("a
-//     slab"; 16 or 32 in the direct-to-LDS variant) at a time, with float4 loads into an R-deep register ring and from there into an S-stage LDS ring that
-//     runs S-1 slabs ahead of the compute wavefronts. One workgroup barrier per slab.
-//   * Compute wavefronts read their MFMA operands from the LDS ring, the next group of 4 chain rows always in flight
-//     while the MFMAs of the current group issue. Rows past C are filled with x = -0 and d_dv = +0: their product is
-//     -0 and acc + (-0) == acc for every acc (including +-0, Inf and NaN), so a partial last slab runs the full 16
-//     steps without changing a bit.
+// Common structure (persistent workgroups; every global access is in long, coalesced streams):
+//   * Work items are (chunk, row group, column group) tiles of 64*RW rows x (block*QW) columns, block = 32 or 16
+//     columns per compute wavefront. Each workgroup takes a contiguous range of items and walks them in order.
+//   * Compute wavefronts (RW x QW of them) each own one 64-row output tile; lane l supplies A = x[n, j, i0 + l].
+//   * Loader wavefronts (LW of them) stream the x and d_dv rows of all the workgroup's items, a slab of chain rows
+//     at a time, into an S-stage LDS ring that runs S-1 slabs ahead of the compute wavefronts; one workgroup barrier
+//     per slab. Compute wavefronts read their MFMA operands from the ring, the next group of 4 chain rows always in
+//     flight while the MFMAs of the current group issue.
 //   * d_u of an item is read by the compute wavefronts in accumulator layout (buffer loads with a scalar row offset)
-//     and d_u + acc is stored at the end of the item (one rounding). DU_AT_END = 0 prefetches it when the item
-//     starts; DU_AT_END = 1 reads it at the end, which saves 32 registers per lane: those instances are built for
-//     6 wavefronts per SIMD (MINW), so two workgroups share a compute unit and overlap each other's phases.
+//     and d_u + acc is stored at the end of the item (one rounding).
+//
+// gx_mfma_kernel (register ring): 32-column wavefronts (two 32x32 blocks stacked along the rows); slabs of 16 rows
+// move through an R-deep register ring of float4 loads into LDS. Rows past C are filled with x = -0 and d_dv = +0:
+// their product is -0 and acc + (-0) == acc for every acc (including +-0, Inf and NaN), so a partial last slab runs
+// the full 16 steps without changing a bit. DU_AT_END = 0 prefetches d_u when the item starts; DU_AT_END = 1 reads
+// it at the end, which saves 32 registers per lane: those instances are built for 6 wavefronts per SIMD (MINW), so
+// two workgroups share a compute unit and overlap each other's phases.
+//
+// gx_mfma_dma_kernel (direct to LDS): slabs of 16 or 32 rows move from memory straight into their LDS stage with
+// buffer_load_dwordx4 ... lds; 32- or 16-column wavefronts; rows past C are skipped, not padded. Its own comment
+// block below has the details.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

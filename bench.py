@@ -38,7 +38,7 @@ def kernel_hash() -> str:
 
 PLAN_KEYS = ("engine", "rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows",
              "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups",
-             "mf_du_at_end", "mf_block")
+             "mf_du_at_end", "mf_block", "mf_stream_du")
 
 
 def kernel_name(plan: dict) -> str:

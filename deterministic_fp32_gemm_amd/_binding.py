@@ -47,7 +47,7 @@ class sdm_gx_plan_t(ctypes.Structure):
                 ("mf_reg_slabs", ctypes.c_int32), ("mf_loader_waves", ctypes.c_int32),
                 ("mf_workgroups", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("mf_du_at_end", ctypes.c_int32),
-                ("mf_block", ctypes.c_int32), ("reserved", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("mf_block", ctypes.c_int32), ("mf_stream_du", ctypes.c_int32), ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -216,13 +216,13 @@ def make_plan(rows_per_wave, cols_per_lane, waves_per_wg, staging=0, xcd_remap=0
 
 
 def make_mfma_plan(row_waves, col_waves, stages=4, reg_slabs=4, loader_waves=4, workgroups=0,
-                   du_at_end=0, block=32, slab_rows=0) -> sdm_gx_plan_t:
+                   du_at_end=0, block=32, slab_rows=0, stream_du=0) -> sdm_gx_plan_t:
     """A caller-made plan for the matrix-core engine (validated by the entry point that receives it)."""
     p = sdm_gx_plan_t()
     p.engine = SDM_GX_ENGINE_MFMA
     p.mf_row_waves, p.mf_col_waves, p.mf_stages = row_waves, col_waves, stages
     p.mf_reg_slabs, p.mf_loader_waves, p.mf_workgroups = reg_slabs, loader_waves, workgroups
-    p.mf_du_at_end, p.mf_block, p.slab_rows = du_at_end, block, slab_rows
+    p.mf_du_at_end, p.mf_block, p.slab_rows, p.mf_stream_du = du_at_end, block, slab_rows, stream_du
     return p
 
 

@@ -193,15 +193,17 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 // Engine: the matrix cores for chunks with 32 <= C and hd <= 128, where their streaming kernel measured fastest
 // (64x64, 64x128 and 128x128 chunks); the vector-ALU chain otherwise (narrow C, where 64-row MFMA tiles would be
 // mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
-//  Matrix cores: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the
-//  32-column MFMA) with slabs moved straight to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages, and
-//  6 or 8 stages are slower); work items of 64 or 128 rows
-//  (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); enough
-//  workgroups for 8 compute wavefronts per compute unit (two per unit for 64x64 items). Stages of 32 chain rows
-//  when each CU holds one workgroup (half the barrier bubbles, which no other workgroup fills), 16 when it holds two
-//  (the chain starts on a smaller first slab). Measured against the register-ring instances with launches replayed
-//  from graphs: 39% faster on 64x64 chunks, 19% on 64x128, 18% on 128x128. A launch whose rows are not 16-byte
-//  aligned runs the same items through the register ring.
+//  Matrix cores, when C and the row stride of d_dv are multiples of 4: 16-column wavefronts
+//  (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the 32-column MFMA) with slabs moved straight
+//  to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages; 6 or 8 stages are slower). Work items of 64 or
+//  128 rows (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); two
+//  workgroups per CU when an item has fewer than 8 compute wavefronts and there are fewer than 4 items per CU, else
+//  one. One workgroup per CU: stages of 32 chain rows (half the barrier bubbles, which no other workgroup fills).
+//  Two: stages of 16 rows (the chain starts on a smaller first slab) and d_u stores with the non-temporal hint (6%
+//  faster on 64x128 chunks; the hint made 128x128 chunks 6% slower with one workgroup per CU). Measured against the
+//  register-ring instances with launches replayed from graphs: 39% faster on 64x64 chunks, 19% on 64x128, 18% on
+//  128x128. Unaligned rows run the launch-selected unaligned-row twins; strides that are not multiples of 4 get the
+//  register-ring kernel's plan (hd <= 128) or the vector-ALU engine.
 //  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
@@ -238,6 +240,8 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU: 32-row stages
                 p.slab_rows = 32;
                 st = complete_plan(&p, nchunks, C, hd, lds_limit);
+            } else {                                            // two per CU: streaming d_u stores
+                p.mf_stream_du = 1;
             }
         } else {                                        // register ring, 32-column wavefronts
             p.mf_block = 32;
@@ -375,6 +379,7 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
         a.hd = static_cast<int32_t>(hd);
         a.nrg = static_cast<int32_t>(g.nrg);
         a.ncg = static_cast<int32_t>(g.ncg);
+        a.stream_du = p.mf_stream_du != 0;
         const hipError_t err = sink(static_cast<const LaunchRec&>(r));
         return err == hipSuccess ? SDM_GX_OK : hip_fail(err);
     }

@@ -22,6 +22,7 @@ struct MfmaArgs {
     int32_t hd;
     int32_t nrg;        // row groups per chunk: ceil(ceil(C / 64) / row_waves)
     int32_t ncg;        // column groups per chunk: ceil(hd / (block * col_waves))
+    int32_t stream_du;  // direct-to-LDS kernel: 1 = d_u stores carry the non-temporal (streaming) hint
 };
 
 struct MfmaEntry {

@@ -48,6 +48,7 @@ typedef float f32x4a __attribute__((ext_vector_type(4), aligned(16)));
 constexpr int kSlabRows = 16;       // chain rows per LDS ring stage
 constexpr int kOperandGroup = 4;    // chain rows whose MFMA operands are read ahead
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, untyped dword access
+constexpr int kNonTemporal = 2;            // buffer instruction cache policy: nt (streaming)
 
 // 4 floats of a row at column g, zero past `lim`; only columns < lim are dereferenced.
 __device__ __forceinline__ f32x4a load4(const float* p, int g, int lim) {
@@ -522,7 +523,12 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
                 cst = cst + 1 == S ? 0 : cst + 1;
             }
             if (DU_AT_END) uload();
-            if (full) {
+            if (full && a.stream_du) {                  // non-temporal hint (nt): written once, not re-read here
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, u[r] + acc[r]), ur, vo,
+                                                          M::row(r) * ld4, kNonTemporal);
+            } else if (full) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, u[r] + acc[r]), ur, vo,

@@ -120,7 +120,8 @@ typedef enum sdm_gx_status {
  *                    4 or 8). Both are exact fma steps; the results do not depend on the choice. Where the layout
  *                    rules out direct-to-LDS slabs, a mf_block 16 plan runs as mf_block 32 with half the column
  *                    wavefronts (mf_col_waves 2 -> 1 ..), register slabs as above
- *   reserved         0
+ *   mf_stream_du     mf_reg_slabs 0: 1 = d_u stores carry the non-temporal (streaming) cache hint; 0 = plain stores.
+ *                    No effect on results.
  * Outputs of the planner / sdm_gx_plan_complete:
  *   lds_bytes      LDS bytes per workgroup (dynamic for the VALU engine, static for the MFMA engine)
  *   wgs_per_cu     workgroups per CU that can be resident (0 if not known)
@@ -143,7 +144,7 @@ typedef struct sdm_gx_plan {
     int32_t wgs_per_cu;
     int32_t mf_du_at_end;
     int32_t mf_block;
-    int32_t reserved;
+    int32_t mf_stream_du;
     int64_t grid;
 } sdm_gx_plan_t;
 

@@ -51,11 +51,12 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "sdm_gx_gemm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
          sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
          offsetof(sdm_gx_launch_t, plan_fused), offsetof(sdm_gx_plan_t, slab_rows),
          offsetof(sdm_gx_plan_t, mf_row_waves), offsetof(sdm_gx_plan_t, mf_workgroups),
-         offsetof(sdm_gx_plan_t, mf_du_at_end), offsetof(sdm_gx_plan_t, mf_block));
+         offsetof(sdm_gx_plan_t, mf_du_at_end), offsetof(sdm_gx_plan_t, mf_block),
+         offsetof(sdm_gx_plan_t, mf_stream_du));
   return 0;
 }
 """)
@@ -66,7 +67,8 @@ int main(void) {
                     g.sdm_gx_launch_t.ti_max.offset, g.sdm_gx_launch_t.plan_step.offset,
                     g.sdm_gx_launch_t.plan_fused.offset, g.sdm_gx_plan_t.slab_rows.offset,
                     g.sdm_gx_plan_t.mf_row_waves.offset, g.sdm_gx_plan_t.mf_workgroups.offset,
-                    g.sdm_gx_plan_t.mf_du_at_end.offset, g.sdm_gx_plan_t.mf_block.offset]
+                    g.sdm_gx_plan_t.mf_du_at_end.offset, g.sdm_gx_plan_t.mf_block.offset,
+                    g.sdm_gx_plan_t.mf_stream_du.offset]
 
 
 def test_strerror_covers_every_code():
@@ -163,6 +165,7 @@ def test_plan_for_emits_supported_plans():
                 assert p.mf_workgroups == (512 if two else 256)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
                 assert p.slab_rows == (32 if p.grid <= 256 else 16)
+                assert p.mf_stream_du == (0 if p.grid <= 256 else 1)
                 assert p.lds_bytes == 16 * 3 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
                 continue
             if p.engine == g.SDM_GX_ENGINE_MFMA:

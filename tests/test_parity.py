@@ -123,7 +123,8 @@ def dma_plans():
                                                                       (2, 4)) for s, lw, wgs in ((4, 1, 3), (8, 2, 0))] \
         + [g.make_mfma_plan(2, 4, 4, 0, 1, 5, 1)] \
         + [g.make_mfma_plan(rw, cw, s, 0, lw, wgs, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
-           for s, lw, wgs, j in ((3, 1, 3, 16), (8, 2, 0, 16), (3, 1, 2, 32))]
+           for s, lw, wgs, j in ((3, 1, 3, 16), (8, 2, 0, 16), (3, 1, 2, 32))] \
+        + [g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 16, 1), g.make_mfma_plan(2, 2, 3, 0, 1, 3, 0, 16, 32, 1)]
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(37, 150, 157, 4), (64, 256, 260, 4), (16, 16, 16, 0), (5, 300, 301, 8),

@@ -12,6 +12,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -29,10 +30,13 @@ KERNEL_SOURCES = ("deterministic_fp32_gemm_amd/csrc/gx_gemm_kernel.hip", "determ
 
 
 def kernel_hash() -> str:
+    """Hash of the kernel sources' code: line comments removed and whitespace collapsed, so that an edit of comments
+    alone keeps a committed counter measurement valid, and any change of code does not."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            code = re.sub(r"\s+", " ", re.sub(r"//[^\n]*", "", f.read()))
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

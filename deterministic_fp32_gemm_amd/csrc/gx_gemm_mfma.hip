@@ -294,16 +294,17 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_kernel(cons
 }
 
 // ---- direct-to-LDS variant ----------------------------------------------------------------------------------------
-// Same work items, compute wavefronts, LDS stage layout and d_u handling as gx_mfma_kernel, but the loader wavefronts
-// move each slab straight from memory into its LDS stage with buffer_load_dwordx4 ... lds (one instruction moves
-// 64 x 16 contiguous bytes of LDS; each lane names its own source). No register ring: up to S - 1 slabs are in
-// flight per workgroup at no register cost, so a compute unit keeps far more bytes in flight than the register ring
-// allows. Needs x and d_dv rows on 16-byte boundaries (checked on the host).
+// Same work items, LDS stage layout (x rows, then d_dv rows) and d_u handling as gx_mfma_kernel, with 32- or
+// 16-column compute wavefronts (MS) and slabs of J = 16 or 32 chain rows; the loader wavefronts move each slab
+// straight from memory into its LDS stage with buffer_load_dwordx4 ... lds (one instruction moves 64 x 16 contiguous
+// bytes of LDS; each lane names its own source). No register ring: up to S - 1 slabs are in flight per workgroup at
+// no register cost. Rows must share one offset from a 16-byte boundary per array (C and ld_dv multiples of 4:
+// checked on the host); ALN selects the instances for rows that are off the boundary.
 //   * Slab q of the workgroup's stream goes to stage q mod S. Tick q: the loader waits (vmcnt) until slab q has landed,
 //     everyone meets at barrier B_q, the compute wavefronts run slab q, and the loader issues slab q + S - 1 into
-//     stage (q - 1) % S, whose reads by the compute wavefronts ended before B_q.
+//     stage (q - 1) mod S, whose reads by the compute wavefronts ended before B_q.
 //   * Out-of-range sources are cut by the buffer bounds (the chunk's extent): nothing outside the chunk is read.
-//     Rows past C in a slab are never used: the last slab of an item runs only its C - 16*s chain steps, so no
+//     Rows past C in a slab are never used: the last slab of an item runs only its C - J*s chain steps, so no
 //     padding value has to be exact. Stale or zero LDS in columns past hd or rows past C only reaches outputs
 //     that are never stored.
 //   * The loader meets the barriers with a bare s_barrier (the compute side's barrier would make the compiler wait

@@ -4,7 +4,8 @@ One benchmark step is one pass of the whole hot path over the workload: the prep
 steps of the workload (by default as one fused launch; --driver per-step issues one launch per step). Inputs are
 synthetic, seeded and resident in device memory before timing starts. Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--driver fused|per-step] [--cold]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--driver fused|per-step|graph] [--cold]
+                  [--plan ...] [--no-cpu] [--cpu-seconds S]
 """
 
 from __future__ import annotations
@@ -12,8 +13,8 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import re
 import os
+import re
 import sys
 import time
 
@@ -80,7 +81,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--plan", default=None,
                     help="override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,REG_SLABS,"
-                         "LOADER_WAVES[,WORKGROUPS[,DU_AT_END]]")
+                         "LOADER_WAVES[,WORKGROUPS[,DU_AT_END[,BLOCK[,SLAB_ROWS[,STREAM_DU]]]]] "
+                         "(REG_SLABS 0: slabs straight to LDS; BLOCK 16 or 32 columns per wavefront)")
     return ap.parse_args()
 
 

@@ -394,6 +394,7 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
     const int nmine = left < a.per ? left : a.per;
     if (nmine <= 0) return;                             // workgroup-uniform: no barrier reached
     const int ns = (C + J - 1) / J;                     // slabs per item
+    const int nfull = C / J;                            // of them holding J chain rows
     const int nch = a.n_items / (a.nrg * a.ncg);        // chunks of the launch
     const int64_t total = static_cast<int64_t>(nmine) * ns;
 
@@ -516,11 +517,18 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
                 }
             };
             if (!DU_AT_END) uload();
-            for (int s = 0; s < ns; ++s) {
+            // full slabs, then the partial last one: two loops, so the accumulator keeps its registers across
+            // slabs (one loop with both paths had the compiler copy it between register sets at every slab)
+            for (int s = 0; s < nfull; ++s) {
                 __syncthreads();                        // B_q: slab q is in LDS
                 const int off = cst * STAGE_FLOATS;
-                if (s * J + J <= C) compute(xs0 + off, ds0 + off);
-                else compute_tail(xs0 + off, ds0 + off, C - s * J);
+                compute(xs0 + off, ds0 + off);
+                cst = cst + 1 == S ? 0 : cst + 1;
+            }
+            if (nfull < ns) {
+                __syncthreads();
+                const int off = cst * STAGE_FLOATS;
+                compute_tail(xs0 + off, ds0 + off, C - nfull * J);
                 cst = cst + 1 == S ? 0 : cst + 1;
             }
             if (DU_AT_END) uload();

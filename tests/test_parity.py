@@ -157,7 +157,8 @@ def test_signed_zero_through_padded_steps(C):
     want = expected(x, dv, du, hd, 0, N)
     assert (np.signbit(want[:, :, :hd])).all() and (want[:, :, :hd] == 0).all()
     plans = [None, g.make_mfma_plan(1, 2, 4, 4, 2), g.make_mfma_plan(2, 1, 4, 2, 4, 1), g.make_plan(1, 1, 2, 1, 1),
-             g.make_mfma_plan(1, 2, 4, 0, 1), g.make_mfma_plan(2, 1, 8, 0, 2, 1)]
+             g.make_mfma_plan(1, 2, 4, 0, 1), g.make_mfma_plan(2, 1, 8, 0, 2, 1),
+             g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 16)]
     for res in ((4, 8, 12), (0, 0, 0)):             # direct-to-LDS slabs need the aligned layout
         case = DeviceCase(x, dv, du, hd, res_u=res[0], res_v=res[1], res_x=res[2])
         for plan in plans:
@@ -167,15 +168,18 @@ def test_signed_zero_through_padded_steps(C):
             assert_matches(got, want, du, hd, f"signed zero C={C} res {res} plan {plan}")
 
 
-def test_mfma_engine_single_rounding():
+@pytest.mark.parametrize("C,plan", [(2, (1, 2, 4, 4, 2)),                                  # 32x32x1, register ring
+                                    (4, (1, 4, 3, 0, 1, 0, 0, 16, 32))])                  # 16x16x1, direct to LDS
+def test_mfma_engine_single_rounding(C, plan):
     """Two-step chains on near-cancelling inputs: acc = fma(x1, d1, fl(x0*d0)), where a fused and an unfused second
-    step round differently for a large share of the outputs. The matrix-core engine (one K=1 MFMA per step) must
-    give the fused result: the oracle's fmaf chain, bit for bit."""
+    step round differently for a large share of the outputs. The matrix-core engine (one K=1 MFMA per step, each
+    MFMA shape) must give the fused result: the oracle's fmaf chain, bit for bit. With C = 4 the chain's last two
+    steps have x = 0 (slabs straight to LDS need C % 4 == 0)."""
     rng = np.random.default_rng(2026)
-    N, P, C, hd = 512, 8, 2, 64
+    N, P, hd = 512, 8, 64
     x = rng.standard_normal((N, C, C)).astype(np.float32)
-    dv = np.empty((N, C, hd), np.float32)
-    dv[:, 0, :] = rng.standard_normal((N, hd)).astype(np.float32)
+    x[:, 2:, :] = 0
+    dv = rng.standard_normal((N, C, hd)).astype(np.float32)
     # row 1 nearly cancels row 0's product for output row 0: x[n,1,0]*dv[n,1,c] ~ -x[n,0,0]*dv[n,0,c]
     dv[:, 1, :] = (-(x[:, 0, 0:1].astype(np.float64) * dv[:, 0, :]) / x[:, 1, 0:1]).astype(np.float32)
     du = np.zeros((N, C, hd), np.float32)
@@ -185,8 +189,8 @@ def test_mfma_engine_single_rounding():
     differ = unfused.view(np.uint32) != want[:, 0, :].view(np.uint32)
     assert differ.mean() > 0.2, differ.mean()                             # the test has teeth
     case = DeviceCase(x, dv, du, hd)
-    got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, g.make_mfma_plan(1, 2, 4, 4, 2))
-    assert_matches(got, want, du, hd, "mfma single rounding")
+    got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, g.make_mfma_plan(*plan))
+    assert_matches(got, want, du, hd, f"mfma single rounding C={C} plan {plan}")
 
 
 @pytest.mark.parametrize("C,hd,ld,res", [(148, 70, 76, (0, 0, 0)), (64, 64, 64, (0, 0, 0)), (128, 128, 128, (4, 0, 0)),

@@ -198,12 +198,13 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 //  to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages; 6 or 8 stages are slower). Work items of 64 or
 //  128 rows (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); two
 //  workgroups per CU when an item has fewer than 8 compute wavefronts and there are fewer than 4 items per CU, else
-//  one. One workgroup per CU: stages of 32 chain rows (half the barrier bubbles, which no other workgroup fills).
-//  Two: stages of 16 rows (the chain starts on a smaller first slab) and d_u stores with the non-temporal hint (6%
-//  faster on 64x128 chunks; the hint made 128x128 chunks 6% slower with one workgroup per CU). Measured against the
-//  register-ring instances with launches replayed from graphs: 39% faster on 64x64 chunks, 19% on 64x128, 18% on
-//  128x128. Unaligned rows run the launch-selected unaligned-row twins; strides that are not multiples of 4 get the
-//  register-ring kernel's plan (hd <= 128) or the vector-ALU engine.
+//  one. One workgroup per CU walking several items: stages of 32 chain rows (half the barrier bubbles, which no
+//  other workgroup fills). One item per workgroup: stages of 16 rows (the chain starts on a smaller first slab: 3%
+//  faster on 64x64 chunks at one item per CU). Two workgroups per CU: stages of 16 rows and d_u stores with the
+//  non-temporal hint (6% faster on 64x128 chunks; the hint made 128x128 chunks 6% slower with one workgroup per
+//  CU). Measured against the register-ring instances with launches replayed from graphs: 39% faster on 64x64
+//  chunks, 19% on 64x128, 18% on 128x128. Unaligned rows run the launch-selected unaligned-row twins; strides that
+//  are not multiples of 4 get the register-ring kernel's plan (hd <= 128) or the vector-ALU engine.
 //  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
@@ -237,9 +238,11 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             p.mf_workgroups = (p.mf_row_waves * p.mf_col_waves < 8 && items < 4 * num_cus ? 2 : 1) * num_cus;
             p.slab_rows = 16;
             st = complete_plan(&p, nchunks, C, hd, lds_limit);
-            if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU: 32-row stages
-                p.slab_rows = 32;
-                st = complete_plan(&p, nchunks, C, hd, lds_limit);
+            if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU
+                if (items > p.grid) {                           // walking several items: 32-row stages
+                    p.slab_rows = 32;
+                    st = complete_plan(&p, nchunks, C, hd, lds_limit);
+                }
             } else {                                            // two per CU: streaming d_u stores
                 p.mf_stream_du = 1;
             }

@@ -154,7 +154,7 @@ def test_plan_for_emits_supported_plans():
             if p.engine == g.SDM_GX_ENGINE_MFMA and dma_ok(C, hd):
                 # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 columns (32 when hd <= 32
                 # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU unless the items are
-                # many (4 or more per CU), 32-row stages when each CU holds one workgroup
+                # many (4 or more per CU), 32-row stages when each CU holds one workgroup that walks several items
                 assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1
                 assert p.mf_row_waves == (2 if C > 64 else 1)
                 wide = hd > 32 and nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) >= 256
@@ -164,7 +164,7 @@ def test_plan_for_emits_supported_plans():
                 two = p.mf_row_waves * p.mf_col_waves < 8 and items < 4 * 256
                 assert p.mf_workgroups == (512 if two else 256)
                 assert p.grid == mfma_grid(items, p.mf_workgroups)
-                assert p.slab_rows == (32 if p.grid <= 256 else 16)
+                assert p.slab_rows == (32 if p.grid <= 256 and items > p.grid else 16)
                 assert p.mf_stream_du == (0 if p.grid <= 256 else 1)
                 assert p.lds_bytes == 16 * 3 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
                 continue

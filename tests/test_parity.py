@@ -82,6 +82,23 @@ def test_workload_bench_launch(key):
     assert_matches(case.result(), want, case.du_h, hd, f"workload {key} fused x3")
 
 
+@pytest.mark.parametrize("key,pattern", [(k, p) for k in (2, 3, 4, 5) for p in inputs.PATTERNS + ("probe_denormal",)
+                                         if p != "normal"], ids=lambda v: str(v))
+def test_workload_bench_launch_patterns(key, pattern):
+    """The benchmark's launch configuration (prepared launch, all T steps in one fused launch, the planner's plan
+    for the whole workload) on the six value patterns and the subnormal-accumulation probe, against the oracle."""
+    import torch
+    w, case = workload_case(key, pattern)
+    say(f"workload {key} pattern {pattern} fused")
+    N, C, hd = w.N, w.C, w.hd
+    step = g.make_step(case.du.view(N, C, w.ld)[:, :, :hd], case.x.view(N, C, C), case.dv.view(N, C, w.ld)[:, :, :hd],
+                       w.P)
+    step.fused(0, w.T)
+    torch.cuda.synchronize()
+    want = expected(case.x_h, case.dv_h, case.du_h, hd, 0, N)
+    assert_matches(case.result(), want, case.du_h, hd, f"workload {key} {pattern} fused")
+
+
 # ---- every plan gives the same bits --------------------------------------------------------------------------------
 def all_plans(C, hd=64):
     """Every plan the library has a kernel instance for (plans without one are rejected by the library): every

@@ -343,10 +343,15 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
         sdm_gx_plan_t q = p;
         if (e->reg_slabs == 0) {
             const sdm_gx::MfmaEntry* twin = nullptr;
-            if (dma_strides_ok(C, ld_dv) && !rows_aligned16(x, dv))      // rows off a 16-byte boundary
-                twin = sdm_gx::find_mfma_kernel(e->row_waves, e->col_waves, e->stages, 0, e->loader_waves,
-                                                e->du_at_end, e->block, e->slab_rows,
-                                                reinterpret_cast<uintptr_t>(x) % 16 == 0 ? 2 : 3);
+            if (dma_strides_ok(C, ld_dv) && !rows_aligned16(x, dv)) {    // rows off a 16-byte boundary
+                // x aligned: d_dv rows by 4-byte DMA (4), else from the 16-byte boundary below (2); x too: 3
+                const bool xa = reinterpret_cast<uintptr_t>(x) % 16 == 0;
+                for (int aln : {xa ? 4 : 3, xa ? 2 : 3}) {
+                    twin = sdm_gx::find_mfma_kernel(e->row_waves, e->col_waves, e->stages, 0, e->loader_waves,
+                                                    e->du_at_end, e->block, e->slab_rows, aln);
+                    if (twin) break;
+                }
+            }
             if (twin) {
                 e = twin;
             } else if (!dma_strides_ok(C, ld_dv) || !rows_aligned16(x, dv)) {

@@ -317,6 +317,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, float* lds,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
+// 4 bytes per lane from buffer offset voff into LDS at lds + 4 * lane (lds wave-uniform)
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, float* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, 0, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {     // s_waitcnt vmcnt(N), other counters unconstrained
     static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
@@ -374,12 +379,16 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
     constexpr int XW = 64 * RW, DW = MS * QW;          // x / d_dv columns of a work item
     // LDS rows: for rows that start 4, 8 or 12 bytes past a 16-byte boundary (ALN bit 0: x, bit 1: d_dv) each row
     // is loaded from the boundary below its start, one more 16-byte group per row; the first `shift` floats of such
-    // an LDS row are then not the row's.
-    constexpr int AX = ALN & 1, AD = (ALN >> 1) & 1;
+    // an LDS row are then not the row's. ALN bit 2 moves such d_dv rows with 4-byte DMA instead: 64 floats per
+    // instruction at any 4-byte offset, LDS rows exactly DW floats (1-3% faster on 64 x 64 items).
+    constexpr int AX = ALN & 1, AD = (ALN >> 1) & 1, D4 = (ALN >> 2) & 1;
+    static_assert(!(AD && D4), "one way of moving unaligned d_dv rows");
+    static_assert(!D4 || (64 % DW == 0 || DW % 64 == 0), "4-byte DMA: rows of a 64-float instruction");
     constexpr int XR = XW + 4 * AX, DR = DW + 4 * AD;            // LDS row widths in floats
     constexpr int GXR = XR / 4, GDR = DR / 4;                    // 16-byte groups per LDS row
-    constexpr int NIX = (J * GXR + 63) / 64, NID = (J * GDR + 63) / 64;   // DMA instructions per slab: x, d_dv
-    constexpr int NI = NIX + NID, GS = NI * 64;         // float4 groups of one stage (with padding lanes)
+    constexpr int NIX = (J * GXR + 63) / 64;                     // DMA instructions per slab: x, d_dv
+    constexpr int NID = D4 ? (J * DW + 63) / 64 : (J * GDR + 63) / 64;
+    constexpr int NI = NIX + NID, GS = NIX * 64 + NID * (D4 ? 16 : 64);   // float4 groups of one stage
     constexpr int PERW = NI / LW;                       // per loader wavefront per slab
     constexpr int K = kOperandGroup;
     constexpr int kNoSource = 0x3FFFFFF0;               // padding lanes: a float offset past every buffer range
@@ -411,6 +420,9 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
             if (k < NIX / LW) {
                 const int g = m * 64 + lane, jj = g / GXR;
                 off[k] = g < J * GXR ? jj * C + (g - jj * GXR) * 4 : kNoSource;
+            } else if (D4) {
+                const int h = (m - NIX) * 64 + lane, jj = h / DW;
+                off[k] = h < J * DW ? jj * static_cast<int>(a.ld_dv) + (h - jj * DW) : kNoSource;
             } else {
                 const int h = (m - NIX) * 64 + lane, jj = h / GDR;
                 off[k] = h < J * GDR ? jj * static_cast<int>(a.ld_dv) + (h - jj * GDR) * 4 : kNoSource;
@@ -435,11 +447,14 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
             float* st = reinterpret_cast<float*>(&ring[stage][0]);
 #pragma unroll
             for (int k = 0; k < PERW; ++k) {
-                float* dst = st + (wl + k * LW) * 256;
+                const int m = wl + k * LW;
                 if (k < NIX / LW)
-                    load_lds16(xr, dst, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
+                    load_lds16(xr, st + m * 256, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
+                else if (D4)
+                    load_lds4(dr, st + NIX * 256 + (m - NIX) * 64,
+                              static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
                 else
-                    load_lds16(dr, dst, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
+                    load_lds16(dr, st + m * 256, static_cast<int>(static_cast<unsigned>(off[k]) * 4u));
             }
             if (++ls == ns) {
                 ls = 0;
@@ -569,12 +584,15 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 // Direct-to-LDS instances (reg_slabs = 0). 32-column tiles: S = 4 stages of 16 chain rows and 1 loader wavefront,
 // and S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
 // workgroups per CU. 16-column tiles: S = 3 stages of 16 or 32 chain rows and 1 loader wavefront (also for rows off
-// a 16-byte boundary, ALN 2: d_dv rows only, ALN 3: x rows too, chosen at launch from the pointers), and S = 8 of
-// 16 rows with 2 loader wavefronts.
+// a 16-byte boundary, chosen at launch from the pointers: ALN 4 d_dv rows by 4-byte DMA, or ALN 2 from the boundary
+// below where 4-byte DMA would exceed the vmcnt range (64 x 128 tiles with 32-row stages); ALN 3 x rows too), and
+// S = 8 of 16 rows with 2 loader wavefronts.
 #define SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, ALN) \
     {RW, QW, S, 0, LW, DE, reinterpret_cast<const void*>(&gx_mfma_dma_kernel<RW, QW, S, LW, DE, MW, MS, J, ALN>), \
-     static_cast<int>(sizeof(f32x4a) * S * 64 * \
-                      ((J * (16 * RW + (ALN & 1)) + 63) / 64 + (J * (MS / 4 * QW + (ALN >> 1)) + 63) / 64)), \
+     static_cast<int>(sizeof(f32x4a) * S * \
+                      (64 * ((J * (16 * RW + (ALN & 1)) + 63) / 64) + \
+                       (ALN & 4 ? 16 * ((J * MS * QW + 63) / 64) \
+                                : 64 * ((J * (MS / 4 * QW + ((ALN >> 1) & 1)) + 63) / 64)))), \
      MS, J, ALN},
 #define SDM_GX_MD(RW, QW, S, LW, DE, MW, MS, J) SDM_GX_MD_A(RW, QW, S, LW, DE, MW, MS, J, 0)
 #define SDM_GX_MD2(RW, QW, MS) SDM_GX_MD(RW, QW, 4, 1, 0, 1, MS, 16) SDM_GX_MD(RW, QW, 8, 2, 0, 1, MS, 16)
@@ -582,11 +600,13 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
     SDM_GX_MD(RW, QW, 3, 1, 0, 1, 16, 32) \
     SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 16, 2) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 32, 2) \
     SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 16, 3) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 32, 3)
+#define SDM_GX_MD4(RW, QW) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 16, 4) SDM_GX_MD_A(RW, QW, 3, 1, 0, 1, 16, 32, 4)
 
 const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)
     SDM_GX_MD2(2, 2, 32) SDM_GX_MD2(2, 4, 32) SDM_GX_MD(2, 4, 4, 1, 1, 5, 32, 16)
     SDM_GX_MD3(1, 2) SDM_GX_MD3(1, 4) SDM_GX_MD3(1, 8) SDM_GX_MD3(2, 2) SDM_GX_MD3(2, 4)
+    SDM_GX_MD4(1, 2) SDM_GX_MD4(1, 4) SDM_GX_MD4(2, 2) SDM_GX_MD4(2, 4) SDM_GX_MD_A(1, 8, 3, 1, 0, 1, 16, 16, 4)
     SDM_GX_MF_RL(1, 1) SDM_GX_MF_RL(1, 2) SDM_GX_MF_RL(1, 4)
     SDM_GX_MF(1, 8, 4, 4, 4) SDM_GX_MF(1, 8, 4, 2, 4) SDM_GX_MF(1, 8, 4, 2, 2)
     SDM_GX_MF_RL(2, 1) SDM_GX_MF_RL(2, 2)

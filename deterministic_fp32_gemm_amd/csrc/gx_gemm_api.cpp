@@ -196,7 +196,8 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 //  Matrix cores, when C and the row stride of d_dv are multiples of 4: 16-column wavefronts
 //  (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the 32-column MFMA) with slabs moved straight
 //  to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages; 6 or 8 stages are slower). Work items of 64 or
-//  128 rows (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle); two
+//  128 rows (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle; 64 rows
+//  by 128 columns when C > 64 and hd is a multiple of 128, with items enough for every CU); two
 //  workgroups per CU when an item has fewer than 8 compute wavefronts and there are fewer than 4 items per CU, else
 //  one. One workgroup per CU walking several items: stages of 32 chain rows (half the barrier bubbles, which no
 //  other workgroup fills). One item per workgroup: stages of 16 rows (the chain starts on a smaller first slab: 3%
@@ -231,6 +232,10 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             p.mf_row_waves = C > 64 ? 2 : 1;
             p.mf_col_waves = hd > 32 ? 4 : 2;
             if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
+            else if (C > 64 && hd % 128 == 0 && nchunks * cdiv(C, 64) * (hd / 128) >= num_cus) {
+                p.mf_row_waves = 1;                     // 64 x 128 items: 2% faster than 128 x 64 at C = hd = 128
+                p.mf_col_waves = 8;
+            }
             p.mf_stages = 3;
             p.mf_reg_slabs = 0;
             p.mf_loader_waves = 1;

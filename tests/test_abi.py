@@ -153,12 +153,14 @@ def test_plan_for_emits_supported_plans():
                                 else g.SDM_GX_ENGINE_VALU)
             if p.engine == g.SDM_GX_ENGINE_MFMA and dma_ok(C, hd):
                 # 16-column wavefronts, slabs straight to LDS, items of 64 or 128 rows by 64 columns (32 when hd <= 32
-                # or when 64-column items would leave CUs idle), 8 compute wavefronts per CU unless the items are
-                # many (4 or more per CU), 32-row stages when each CU holds one workgroup that walks several items
+                # or when 64-column items would leave CUs idle; 64 x 128 when C > 64 and hd is a multiple of 128 with
+                # items for every CU), 8 compute wavefronts per CU unless the items are many (4 or more per CU),
+                # 32-row stages when each CU holds one workgroup that walks several items
                 assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1
-                assert p.mf_row_waves == (2 if C > 64 else 1)
-                wide = hd > 32 and nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) >= 256
-                assert p.mf_col_waves == (4 if wide else 2)
+                rw0 = 2 if C > 64 else 1
+                wide = hd > 32 and nchunks * cdiv(C, 64 * rw0) * cdiv(hd, 64) >= 256
+                long_rows = wide and C > 64 and hd % 128 == 0 and nchunks * cdiv(C, 64) * (hd // 128) >= 256
+                assert (p.mf_row_waves, p.mf_col_waves) == ((1, 8) if long_rows else (rw0, 4 if wide else 2))
                 assert p.mf_du_at_end == 0
                 items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves)
                 two = p.mf_row_waves * p.mf_col_waves < 8 and items < 4 * 256

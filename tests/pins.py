@@ -95,7 +95,7 @@ def pin_integer(lib=None):
 # ---- pin 3: zero x ------------------------------------------------------------------------------------------------
 def pin_zero_x(lib=None):
     N, P, ti, C, hd, ld = 4, 2, 1, 9, 6, 8
-    _, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_normal", seed=3)   # finite, with signed zeros
+    _, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_signed_zero", seed=3)   # finite, with signed zeros
     x = np.zeros((N, C, C), np.float32)
     x.reshape(-1)[::3] = -0.0
     got = du.copy()
@@ -118,7 +118,7 @@ def pin_zero_x(lib=None):
 # ---- pin 4: identity x --------------------------------------------------------------------------------------------
 def pin_identity_x(lib=None):
     N, P, ti, C, hd, ld = 3, 1, 2, 7, 5, 5
-    _, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_normal", seed=4)
+    _, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_signed_zero", seed=4)
     x = np.broadcast_to(np.eye(C, dtype=np.float32), (N, C, C)).copy()
     got = du.copy()
     oracle.gx_gemm_step(got, x, dv, ti, P, hd, lib=lib)
@@ -201,7 +201,37 @@ def pin_error_bound(lib=None):
         raise PinFailure("result equals float64 evaluation rounded once: the chain is not binary32")
 
 
-ALL_PINS = (pin_golden, pin_integer, pin_zero_x, pin_identity_x, pin_exact, pin_error_bound)
+# ---- pin 7: the floating-point environment guard ----------------------------------------------------------------
+def pin_fpenv_refusal(lib=None):
+    """The oracle's results are IEEE binary32 with subnormals kept and round-to-nearest-even, the page's setting
+    (plain fmaf and +; its qualification probe feeds subnormal accumulations). A host thread in flush-to-zero,
+    denormals-are-zero or a directed rounding mode would silently give other bits, so the oracle must refuse there:
+    the guard reports the environment as unusable, the step returns its environment status without touching d_u,
+    and it runs again once the environment is restored. Each mode is entered alone, so every check of the guard is
+    exercised on its own."""
+    from tests import fpenv
+    x, dv, du = inputs.shape_inputs(2, 4, 3, None, "hazard_subnormal", seed=8)
+    for m in fpenv.MODES:
+        got = du.copy()
+        with fpenv.mode(m):
+            usable = oracle.fpenv_ok(lib)
+            try:
+                oracle.gx_gemm_step(got, x, dv, 0, 2, lib=lib)
+                refused = False
+            except RuntimeError:
+                refused = True
+        if usable:
+            raise PinFailure(f"fpenv guard: reports the host usable in mode {m}")
+        if not refused:
+            raise PinFailure(f"fpenv guard: the step ran in mode {m}")
+        _check(same_bits(got, du), got, du, f"fpenv guard: d_u written while refusing in mode {m}")
+    if not oracle.fpenv_ok(lib):
+        raise PinFailure("fpenv guard: refuses the restored IEEE environment")
+    got = du.copy()
+    oracle.gx_gemm_step(got, x, dv, 0, 2, lib=lib)
+
+
+ALL_PINS = (pin_golden, pin_integer, pin_zero_x, pin_identity_x, pin_exact, pin_error_bound, pin_fpenv_refusal)
 
 
 def run_all(lib=None) -> dict:

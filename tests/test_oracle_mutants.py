@@ -31,6 +31,11 @@ MUTANTS = {
     "wrong_step_index": [("const int64_t n = ti * P + p;", "const int64_t n = ti + p;")],
     "ignores_row_stride": [("d_dv[(n * C + j) * ld_dv + c]", "d_dv[(n * C + j) * hd + c]")],
     "writes_padding": [("for (int64_t c = 0; c < hd; ++c) {", "for (int64_t c = 0; c < ld_u; ++c) {")],
+    "guard_never_refuses": [("    if (!sdm_gx_oracle_fpenv_ok()) return ORACLE_BAD_FPENV;\n", "")],
+    "guard_ignores_flush_to_zero": [("    if (csr & (1u << 15)) return 0;\n", "")],
+    "guard_ignores_denormals_are_zero": [("    if (csr & (1u << 6)) return 0;\n", "")],
+    "guard_ignores_sse_rounding": [("    if (csr & (3u << 13)) return 0;\n", "")],
+    "guard_ignores_c_rounding": [("    if (fegetround() != FE_TONEAREST) return 0;\n", "")],
     "first_product_start": [("float acc = +0.0f;\n                for (int64_t j = 0; j < C; ++j) {",
                              "float acc = x[(n * C) * C + i] * d_dv[(n * C) * ld_dv + c];\n"
                              "                for (int64_t j = 1; j < C; ++j) {")],

@@ -7,11 +7,11 @@ the HIP library nor the oracle. Every array is numpy float32 on the host:
   d_dv (N, C, ld)      columns c < hd are data, columns hd..ld-1 hold PAD_BITS
   d_u  (N, C, ld)      same layout as d_dv
 
-Workloads (the five shapes the update is measured and checked on) and value patterns follow the recipes stated in
-the repository's design notes; the page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py"
-contributes its qualification probe's pattern families (_probe_inputs: signed zeros, half-zero masks, wide
-exponents with near-overflow spikes, subnormal accumulation, near-cancelling row pairs, scattered specials), which
-are re-drawn here with numpy's generator rather than reproduced bit for bit.
+Workloads (the five shapes the update is measured and checked on) and the six value patterns follow the recipes
+stated in the repository's design notes. The hazard families target the same floating-point hazards as the
+qualification probe on the page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py" (signed
+zeros, sparse operands, wide exponents with overflow, subnormal accumulation, cancellation, special values); their
+recipes (rates, scales, structure) are this module's own.
 """
 
 from __future__ import annotations
@@ -65,9 +65,11 @@ WORKLOADS = {
 
 # The six value patterns every step is checked on.
 PATTERNS = ("normal", "zeros", "large", "denormal", "inf", "nan")
-# The qualification probe's pattern families, re-drawn.
-PROBE_PATTERNS = ("probe_normal", "probe_zeros", "probe_large", "probe_denormal", "probe_cancel", "probe_special")
-ALL_PATTERNS = PATTERNS + PROBE_PATTERNS
+# Hazard families, one floating-point hazard of the chain each (the same hazards the page's qualification probe
+# targets; these recipes are this module's own).
+HAZARD_PATTERNS = ("hazard_signed_zero", "hazard_sparse", "hazard_wide", "hazard_subnormal", "hazard_cancel",
+                   "hazard_special")
+ALL_PATTERNS = PATTERNS + HAZARD_PATTERNS
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -123,51 +125,89 @@ def raw(N: int, C: int, hd: int, pattern: str, seed_key: tuple, dist: str = "nor
         for a in arrs:
             _inject(rng, a, 0.01, vals)
         return tuple(_f32(a) for a in arrs)
-    if pattern.startswith("probe_"):
-        return _probe(rng, N, C, hd, pattern[len("probe_"):])
+    if pattern.startswith("hazard_"):
+        return _hazard(rng, N, C, hd, pattern[len("hazard_"):])
     raise ValueError(f"unknown pattern {pattern!r}")
 
 
-def _probe(rng, N, C, hd, kind):
-    x = rng.standard_normal((N, C, C)).astype(np.float32) * np.float32(0.25)
-    dv = rng.standard_normal((N, C, hd)).astype(np.float32)
-    du = rng.standard_normal((N, C, hd)).astype(np.float32)
-    if kind == "normal":                  # signed zeros sprinkled at fixed strides
-        x.reshape(-1)[::7] = -0.0
-        dv.reshape(-1)[::11] = 0.0
-        du.reshape(-1)[::13] = -0.0
-    elif kind == "zeros":                 # half of the entries zero, x's zeros negative
-        x *= (rng.random(x.shape) < 0.5)
-        x[x == 0] = -0.0
-        dv *= (rng.random(dv.shape) < 0.5)
-        du[rng.random(du.shape) < 0.5] = -0.0
-    elif kind == "large":                 # exponents spread over 2^-60 .. 2^60, near-overflow spikes
-        for a in (x, dv, du):
-            a *= np.exp2(rng.integers(-60, 61, size=a.shape)).astype(np.float32)
-        x.reshape(-1)[::17] = 3.0e38
-        dv.reshape(-1)[::19] = -3.0e38
-    elif kind == "denormal":              # products land in the subnormal range and accumulate there
-        x *= np.float32(1e-20)
-        dv *= np.float32(1e-19)
-        du *= np.float32(1e-38)
-        du.reshape(-1)[::5] = np.float32(1e-41)
-    elif kind == "cancel":                # odd rows of d_dv nearly cancel the even rows above them
-        x = (np.sign(rng.standard_normal(x.shape)) * (1.0 + rng.random(x.shape))).astype(np.float32)
-        dv *= np.float32(1e4)
+def _signs(rng, shape) -> np.ndarray:
+    return np.where(rng.random(shape) < 0.5, np.float32(-1.0), np.float32(1.0))
+
+
+def _hazard(rng, N, C, hd, kind):
+    """Inputs that stress one floating-point hazard of the fixed chain at a time (x, d_dv, d_u)."""
+    sx, sv, su = (N, C, C), (N, C, hd), (N, C, hd)
+    if kind == "signed_zero":
+        # N(0,1) with one element in eight replaced by a zero of random sign: -0 products meet +0 and -0 sums
+        out = []
+        for s in (sx, sv, su):
+            a = rng.standard_normal(s, dtype=np.float32)
+            z = rng.random(s) < 0.125
+            a[z] = np.float32(0.0) * _signs(rng, s)[z]
+            out.append(a)
+        return tuple(out)
+    if kind == "sparse":
+        # most products vanish: x zero (random sign) with probability 0.6, d_dv with 0.3, d_u is -0 with 0.3
+        x = rng.standard_normal(sx, dtype=np.float32)
+        x = np.where(rng.random(sx) < 0.6, np.float32(0.0) * _signs(rng, sx), x)
+        dv = rng.standard_normal(sv, dtype=np.float32)
+        dv = np.where(rng.random(sv) < 0.3, np.float32(0.0) * _signs(rng, sv), dv)
+        du = rng.standard_normal(su, dtype=np.float32)
+        du = np.where(rng.random(su) < 0.3, np.float32(-0.0), du)
+        return _f32(x), _f32(dv), _f32(du)
+    if kind == "wide":
+        # sign * m * 2^e, m in [1, 2): x and d_dv exponents over [-70, 70] (products from the subnormal range to
+        # overflow), d_u over [-40, 40]; one x and d_dv element in 500 at +-m * 2^126 (overflows against most rows)
+        def draw(s, lo, hi):
+            m = (1.0 + rng.random(s)) * _signs(rng, s)
+            return _f32(np.ldexp(m, rng.integers(lo, hi + 1, size=s)))
+        x, dv, du = draw(sx, -70, 70), draw(sv, -70, 70), draw(su, -40, 40)
+        for a in (x, dv):
+            flat = a.reshape(-1)
+            k = max(1, flat.size // 500)
+            idx = rng.choice(flat.size, size=k, replace=False)
+            flat[idx] = _f32(np.ldexp((1.0 + rng.random(k)) * _signs(rng, k), 126))
+        return x, dv, du
+    if kind == "subnormal":
+        # every product is subnormal (|x d| about 2^-132) and the chain accumulates below 2^-126; d_u subnormal,
+        # with one element in seven at k * 2^-149 (k = 1 .. 7, the smallest subnormals)
+        x = _f32(np.ldexp(rng.standard_normal(sx), -64))
+        dv = _f32(np.ldexp(rng.standard_normal(sv), -68))
+        du = _f32(np.ldexp(rng.standard_normal(su), -128))
+        flat = du.reshape(-1)
+        idx = np.flatnonzero(rng.random(flat.size) < 1.0 / 7.0)
+        flat[idx] = _f32(np.ldexp(rng.integers(1, 8, size=idx.size) * _signs(rng, idx.size), -149))
+        return x, dv, du
+    if kind == "cancel":
+        # mirrored chain rows: row C-1-j of x repeats row j and row C-1-j of d_dv is row j negated and perturbed
+        # by a relative 2^-11 or less, so the late half of every chain undoes the early half (magnitudes near 2^12)
+        # and what is left depends on the order of the steps
+        x = _f32(rng.choice(np.array([0.5, 1.0, 1.5, 2.0], np.float32), size=sx) * _signs(rng, sx))
+        dv = _f32(np.ldexp(rng.standard_normal(sv), 12))
         h = C // 2
         if h:
-            jitter = (1.0 + 1e-3 * rng.standard_normal((N, h, hd))).astype(np.float32)
-            dv[:, 1:2 * h:2, :] = -dv[:, 0:2 * h:2, :] * jitter
-        du *= np.float32(1e-3)
-    elif kind == "special":               # NaN, +-Inf, -0, a subnormal and +-near-max at random slots
-        specials = np.array([np.nan, np.inf, -np.inf, -0.0, 1e-41, 3.4e38, -3.4e38], dtype=np.float32)
-        for a, k in ((dv, 64), (x, 16), (du, 32)):
+            lo = np.arange(h)
+            hi = C - 1 - lo
+            x[:, hi, :] = x[:, lo, :]
+            delta = _f32(1.0 + np.ldexp(rng.uniform(-1.0, 1.0, size=(N, h, hd)), -11))
+            dv[:, hi, :] = -dv[:, lo, :] * delta
+        du = _f32(np.ldexp(rng.standard_normal(su), -6))
+        return _f32(x), _f32(dv), du
+    if kind == "special":
+        # N(0,1) with scattered specials: quiet NaNs (two payloads), +-Inf, +-0, +-2^-149, +-FLT_MAX, 2^-126; one
+        # element in 256 of d_dv, 384 of d_u, 512 of x (at least one each)
+        vals = np.array([0x7FC00000, 0xFFC12345, 0x7F800000, 0xFF800000, 0x00000000, 0x80000000, 0x00000001,
+                         0x80000001, 0x7F7FFFFF, 0xFF7FFFFF, 0x00800000], dtype=np.uint32).view(np.float32)
+        out = []
+        for s, every in ((sx, 512), (sv, 256), (su, 384)):
+            a = rng.standard_normal(s, dtype=np.float32)
             flat = a.reshape(-1)
-            k = min(k, flat.size)
-            flat[rng.permutation(flat.size)[:k]] = specials[np.arange(k) % specials.size]
-    else:
-        raise ValueError(kind)
-    return _f32(x), _f32(dv), _f32(du)
+            k = max(1, flat.size // every)
+            idx = rng.choice(flat.size, size=k, replace=False)
+            flat[idx] = vals[rng.integers(0, vals.size, size=k)]
+            out.append(a)
+        return tuple(out)
+    raise ValueError(kind)
 
 
 def workload_inputs(w: Workload | int, pattern: str = "normal"):

@@ -110,7 +110,7 @@ def qualify(cases=DEFAULT_CASES, patterns=None, backends=("rocblas", "torch"), N
 
     from .step import aligned_empty
 
-    patterns = patterns or (inputs.PATTERNS + inputs.PROBE_PATTERNS)
+    patterns = patterns or (inputs.PATTERNS + inputs.HAZARD_PATTERNS)
     rows = []
     for C, hd, ld, res in cases:
         for pattern in patterns:

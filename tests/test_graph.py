@@ -24,7 +24,7 @@ SHAPES = [  # N, P, C, hd, ld, residues, engine expected from the planner
 @pytest.mark.parametrize("mode", [g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_REVERSE, g.SDM_GX_STEPS_FUSED])
 def test_graph_replays_match_the_oracle(N, P, C, hd, ld, res, engine, mode):
     import torch
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=N + C + hd + mode)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_cancel", seed=N + C + hd + mode)
     case = DeviceCase(x, dv, du, hd, res_u=res[0], res_x=res[1], res_v=res[2])
     step = g.make_step(case.du.view(N, C, ld)[:, :, :hd], case.x.view(N, C, C), case.dv.view(N, C, ld)[:, :, :hd], P)
     assert step.geom["fused"]["engine"] == engine

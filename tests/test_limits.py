@@ -27,7 +27,7 @@ assert (C + 32) * LD_U * 4 >= 1 << 31                 # with ld_dv = LD_U, slabs
 
 @pytest.fixture(scope="module")
 def host_inputs():
-    x, dv, du = inputs.shape_inputs(N, C, HD, HD, "probe_cancel", seed=2031)
+    x, dv, du = inputs.shape_inputs(N, C, HD, HD, "hazard_cancel", seed=2031)
     return x, dv, du, expected(x, dv, du, HD, 0, N)
 
 

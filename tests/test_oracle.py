@@ -61,7 +61,7 @@ def test_exact_rounding_helper_against_known_values():
 def test_step_order_and_chunk_split_invariance(oracle_lib):
     """Steps update disjoint chunks: forward, reverse and all-chunks-at-once (threaded) give identical bits."""
     w = inputs.Workload(0, 6, 3, 12, 10, 13, 0, "normal", "invariance")
-    x, dv, du = inputs.shape_inputs(w.N, w.C, w.hd, w.ld, "probe_cancel", seed=11)
+    x, dv, du = inputs.shape_inputs(w.N, w.C, w.hd, w.ld, "hazard_cancel", seed=11)
     fwd, rev, once = du.copy(), du.copy(), du.copy()
     oracle.gx_gemm_steps(fwd, x, dv, w.P, range(w.T), w.hd, lib=oracle_lib)
     oracle.gx_gemm_steps(rev, x, dv, w.P, reversed(range(w.T)), w.hd, lib=oracle_lib)
@@ -74,7 +74,7 @@ def test_step_order_and_chunk_split_invariance(oracle_lib):
 def test_reversed_chain_differs_on_cancellation(oracle_lib):
     """Negative control: running the chain in reversed j order (by reversing the j axis of x and d_dv) changes bits
     on cancellation-heavy input, so the j order is material and the pins can see it."""
-    x, dv, du = inputs.shape_inputs(4, 32, 16, None, "probe_cancel", seed=12)
+    x, dv, du = inputs.shape_inputs(4, 32, 16, None, "hazard_cancel", seed=12)
     fwd, rev = du.copy(), du.copy()
     oracle.gx_gemm_step(fwd, x, dv, 0, 4, lib=oracle_lib)
     oracle.gx_gemm_step(rev, np.ascontiguousarray(x[:, ::-1, :]), np.ascontiguousarray(dv[:, ::-1, :]), 0, 4,

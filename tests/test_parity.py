@@ -34,8 +34,8 @@ def run_steps(case: DeviceCase, P, ti_begin, ti_end, mode, plan=None):
 
 # ---- the five workloads ----------------------------------------------------------------------------------------------
 WORKLOAD_PATTERNS = [(1, p) for p in inputs.ALL_PATTERNS] + [(2, p) for p in inputs.ALL_PATTERNS] + \
-    [(3, p) for p in inputs.ALL_PATTERNS] + [(4, "normal"), (4, "probe_special"), (4, "probe_denormal")] + \
-    [(5, "normal"), (5, "probe_special"), (5, "nan")]
+    [(3, p) for p in inputs.ALL_PATTERNS] + [(4, "normal"), (4, "hazard_special"), (4, "hazard_subnormal")] + \
+    [(5, "normal"), (5, "hazard_special"), (5, "nan")]
 
 
 @pytest.mark.parametrize("key,pattern", WORKLOAD_PATTERNS, ids=lambda v: str(v))
@@ -82,7 +82,7 @@ def test_workload_bench_launch(key):
     assert_matches(case.result(), want, case.du_h, hd, f"workload {key} fused x3")
 
 
-@pytest.mark.parametrize("key,pattern", [(k, p) for k in (2, 3, 4, 5) for p in inputs.PATTERNS + ("probe_denormal",)
+@pytest.mark.parametrize("key,pattern", [(k, p) for k in (2, 3, 4, 5) for p in inputs.PATTERNS + ("hazard_subnormal",)
                                          if p != "normal"], ids=lambda v: str(v))
 def test_workload_bench_launch_patterns(key, pattern):
     """The benchmark's launch configuration (prepared launch, all T steps in one fused launch, the planner's plan
@@ -148,7 +148,7 @@ def dma_plans():
                                         (100, 72, 76, 0), (36, 40, 44, 0)])
 def test_every_plan_is_bit_identical(C, hd, ld, res):
     N, P = 6, 3
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C + hd)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_cancel", seed=C + hd)
     case = DeviceCase(x, dv, du, hd, res_u=res, res_v=res, res_x=(res * 3) % 256)
     want = expected(x, dv, du, hd, 0, N)
     n = 0
@@ -221,7 +221,7 @@ def test_mfma_direct_to_lds_plans(C, hd, ld, res):
     skip the first floats of each LDS row (the unaligned-row instances); with ld 131 the rows cannot share one offset
     and the launch takes the register ring. Same bits in every case."""
     N, P = 12, 4
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=C * 3 + hd)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_cancel", seed=C * 3 + hd)
     case = DeviceCase(x, dv, du, hd, res_u=res[0], res_v=res[1], res_x=res[2])
     want = expected(x, dv, du, hd, 0, N)
     for plan in dma_plans():
@@ -261,7 +261,7 @@ def test_mfma_engine_many_items_per_workgroup():
     """Persistent matrix-core workgroups walking long ranges of work items (chunks x row groups x column groups),
     ragged in rows and columns, per step and fused."""
     N, P, C, hd, ld = 30, 5, 150, 70, 73
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_cancel", seed=77)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_cancel", seed=77)
     case = DeviceCase(x, dv, du, hd, res_u=4, res_v=0, res_x=8)
     want = expected(x, dv, du, hd, 0, N)
     for plan in (g.make_mfma_plan(2, 2, 4, 4, 4, 3), g.make_mfma_plan(1, 1, 4, 2, 2, 7),
@@ -277,7 +277,7 @@ def test_mfma_engine_many_items_per_workgroup():
 # ---- driver modes ----------------------------------------------------------------------------------------------------
 def test_driver_modes_agree():
     N, P, C, hd, ld = 14, 4, 24, 70, 72              # N % P != 0: chunks 12, 13 belong to no step
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "probe_large", seed=5)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_wide", seed=5)
     case = DeviceCase(x, dv, du, hd, res_u=12, res_v=20, res_x=4)
     want = expected(x, dv, du, hd, 0, (N // P) * P)
     for mode in (g.SDM_GX_STEPS_FORWARD, g.SDM_GX_STEPS_REVERSE, g.SDM_GX_STEPS_FUSED):
@@ -313,13 +313,13 @@ def test_contiguous_entry_point():
 # ---- edge shapes and alignment -------------------------------------------------------------------------------------
 EDGE = [  # N, P, C, hd, ld, res_u, res_x, res_v, pattern
     (1, 1, 1, 1, 1, 0, 0, 0, "normal"),
-    (2, 1, 1, 5, 7, 4, 8, 12, "probe_special"),
+    (2, 1, 1, 5, 7, 4, 8, 12, "hazard_special"),
     (3, 3, 3, 5, 5, 4, 4, 4, "normal"),
     (2, 2, 256, 1, 1, 0, 0, 0, "normal"),            # longest chain, one column
-    (2, 2, 256, 260, 263, 4, 0, 8, "probe_cancel"),  # longest chain, ragged columns
+    (2, 2, 256, 260, 263, 4, 0, 8, "hazard_cancel"),  # longest chain, ragged columns
     (4, 2, 17, 4100, 4100, 0, 0, 0, "normal"),       # many column blocks with a tail
-    (5, 2, 63, 129, 131, 252, 248, 244, "probe_zeros"),
-    (7, 7, 100, 3, 3, 8, 4, 0, "probe_denormal"),
+    (5, 2, 63, 129, 131, 252, 248, 244, "hazard_sparse"),
+    (7, 7, 100, 3, 3, 8, 4, 0, "hazard_subnormal"),
     (3, 1, 33, 255, 255, 4, 4, 4, "inf"),
 ]
 
@@ -349,7 +349,7 @@ def test_alignment_classes(res):
 
 
 def test_repeated_runs_are_identical():
-    w, case = workload_case(3, "probe_cancel")
+    w, case = workload_case(3, "hazard_cancel")
     first = run_steps(case, w.P, 0, w.T, g.SDM_GX_STEPS_FUSED)
     for _ in range(3):
         case.reset()

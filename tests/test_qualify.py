@@ -19,7 +19,7 @@ def test_vendor_blas_qualification_report():
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
     say(f"rocBLAS {qualify.rocblas_version()}")
-    patterns = ("normal", "zeros", "large", "probe_cancel", "probe_denormal", "nan")
+    patterns = ("normal", "zeros", "large", "hazard_cancel", "hazard_subnormal", "nan")
     rows = qualify.qualify(cases=CASES, patterns=patterns)
     assert len(rows) == len(CASES) * len(patterns) * 2
     for r in rows:

@@ -39,7 +39,7 @@ def random_cases(n, seed):
 @pytest.mark.parametrize("case", random_cases(40, 20261202), ids=lambda c: f"case{c[0]}")
 def test_random_shape(case):
     k, N, P, C, hd, ld, res, plan, mode = case
-    x, dv, du = inputs.shape_inputs(N, C, hd, ld, ("normal", "probe_cancel", "probe_special")[k % 3], seed=1000 + k)
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, ("normal", "hazard_cancel", "hazard_special")[k % 3], seed=1000 + k)
     dc = DeviceCase(x, dv, du, hd, res_u=res[0], res_x=res[1], res_v=res[2])
     p = None
     if plan is not None:

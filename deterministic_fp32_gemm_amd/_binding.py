@@ -47,7 +47,8 @@ class sdm_gx_plan_t(ctypes.Structure):
                 ("mf_reg_slabs", ctypes.c_int32), ("mf_loader_waves", ctypes.c_int32),
                 ("mf_workgroups", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("mf_du_at_end", ctypes.c_int32),
-                ("mf_block", ctypes.c_int32), ("mf_stream_du", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("mf_block", ctypes.c_int32), ("mf_stream_du", ctypes.c_int32), ("mf_aln", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -97,9 +98,9 @@ def load() -> ctypes.CDLL:
             "sdm_gx_gemm_ex": [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _PP, _vp],
             "sdm_gx_gemm_steps": [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _PP, _vp],
             "sdm_gx_check": [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64],
-            "sdm_gx_plan": [_i64, _i64, _i64, _i32, _PP],
-            "sdm_gx_plan_for": [_i64, _i64, _i64, _i32, _i32, _PP],
-            "sdm_gx_plan_complete": [_PP, _i64, _i64, _i64, _i32],
+            "sdm_gx_plan": [_i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _PP],
+            "sdm_gx_plan_for": [_i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _PP],
+            "sdm_gx_plan_complete": [_PP, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32],
             "sdm_gx_prepare": [_LP, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _PP],
             "sdm_gx_launch": [_LP, _i64, _vp],
             "sdm_gx_launch_fused": [_LP, _i64, _i64, _vp],
@@ -193,16 +194,21 @@ def sdm_gx_check(d_u, ld_u, x, d_dv, ld_dv, N, ti, P, C, hd) -> int:
                                int(ti), int(P), int(C), int(hd))
 
 
-def sdm_gx_plan(nchunks, C, hd, device=-1) -> sdm_gx_plan_t:
+def sdm_gx_plan(nchunks, C, hd, ld_u=None, ld_dv=None, x_mod16=0, dv_mod16=0, engine=-1, device=-1) -> sdm_gx_plan_t:
+    """The plan a launch with these strides (default: hd) and placements (address mod 16 of x and d_dv) runs."""
     p = sdm_gx_plan_t()
-    _raise(load().sdm_gx_plan(int(nchunks), int(C), int(hd), int(device), ctypes.byref(p)), "sdm_gx_plan")
+    _raise(load().sdm_gx_plan(int(nchunks), int(C), int(hd), int(hd if ld_u is None else ld_u),
+                              int(hd if ld_dv is None else ld_dv), int(x_mod16), int(dv_mod16), int(engine),
+                              int(device), ctypes.byref(p)), "sdm_gx_plan")
     return p
 
 
-def sdm_gx_plan_for(nchunks, C, hd, num_cus=256, lds_per_cu=160 * 1024) -> sdm_gx_plan_t:
+def sdm_gx_plan_for(nchunks, C, hd, num_cus=256, lds_per_cu=160 * 1024, ld_u=None, ld_dv=None, x_mod16=0,
+                    dv_mod16=0, engine=-1) -> sdm_gx_plan_t:
     p = sdm_gx_plan_t()
-    _raise(load().sdm_gx_plan_for(int(nchunks), int(C), int(hd), int(num_cus), int(lds_per_cu), ctypes.byref(p)),
-           "sdm_gx_plan_for")
+    _raise(load().sdm_gx_plan_for(int(nchunks), int(C), int(hd), int(hd if ld_u is None else ld_u),
+                                  int(hd if ld_dv is None else ld_dv), int(x_mod16), int(dv_mod16), int(engine),
+                                  int(num_cus), int(lds_per_cu), ctypes.byref(p)), "sdm_gx_plan_for")
     return p
 
 
@@ -226,9 +232,11 @@ def make_mfma_plan(row_waves, col_waves, stages=4, reg_slabs=4, loader_waves=4, 
     return p
 
 
-def sdm_gx_plan_complete(plan: sdm_gx_plan_t, nchunks, C, hd, lds_per_cu=160 * 1024) -> sdm_gx_plan_t:
-    _raise(load().sdm_gx_plan_complete(ctypes.byref(plan), int(nchunks), int(C), int(hd), int(lds_per_cu)),
-           "sdm_gx_plan_complete")
+def sdm_gx_plan_complete(plan: sdm_gx_plan_t, nchunks, C, hd, lds_per_cu=160 * 1024, ld_u=None, ld_dv=None,
+                         x_mod16=0, dv_mod16=0) -> sdm_gx_plan_t:
+    _raise(load().sdm_gx_plan_complete(ctypes.byref(plan), int(nchunks), int(C), int(hd),
+                                       int(hd if ld_u is None else ld_u), int(hd if ld_dv is None else ld_dv),
+                                       int(x_mod16), int(dv_mod16), int(lds_per_cu)), "sdm_gx_plan_complete")
     return plan
 
 

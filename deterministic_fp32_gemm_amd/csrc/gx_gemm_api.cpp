@@ -128,7 +128,19 @@ constexpr int kDefaultCus = 256;                // MI355X
 const sdm_gx::MfmaEntry* find_mfma(const sdm_gx_plan_t& p) {
     return sdm_gx::find_mfma_kernel(p.mf_row_waves, p.mf_col_waves, p.mf_stages, p.mf_reg_slabs, p.mf_loader_waves,
                                     p.mf_du_at_end, p.mf_block > 0 ? p.mf_block : 32,
-                                    p.slab_rows > 0 ? p.slab_rows : 16, 0);
+                                    p.slab_rows > 0 ? p.slab_rows : 16, p.mf_aln);
+}
+
+// Row strides and the placement of x and d_dv relative to a 16-byte boundary: what decides, besides the shape, which
+// kernel instance a launch runs.
+struct Layout {
+    int64_t ld_u, ld_dv;
+    int x_mod16, dv_mod16;      // base address mod 16, in bytes (0, 4, 8 or 12)
+};
+
+Layout layout_of(int64_t ld_u, int64_t ld_dv, const float* x, const float* dv) {
+    return Layout{ld_u, ld_dv, static_cast<int>(reinterpret_cast<uintptr_t>(x) & 15u),
+                  static_cast<int>(reinterpret_cast<uintptr_t>(dv) & 15u)};
 }
 
 // Geometry of the matrix-core engine for nchunks chunks: work items and the persistent grid.
@@ -154,6 +166,7 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
         if (p->mf_workgroups < 0) return SDM_GX_ERR_PLAN;
         if (p->mf_block == 0) p->mf_block = 32;
         if (p->slab_rows == 0) p->slab_rows = 16;
+        if (p->mf_reg_slabs != 0) p->mf_aln = 0;
         const sdm_gx::MfmaEntry* e = find_mfma(*p);
         if (!e) return SDM_GX_ERR_PLAN;
         p->lds_bytes = e->lds_bytes;
@@ -164,6 +177,7 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
         return SDM_GX_OK;
     }
     if (p->engine != SDM_GX_ENGINE_VALU) return SDM_GX_ERR_PLAN;
+    p->mf_aln = 0;
     if (!valid_ri(p->rows_per_wave) || !valid_rc(p->cols_per_lane) || !valid_waves(p->waves_per_wg))
         return SDM_GX_ERR_PLAN;
     if (p->staging != 0 && p->staging != 1) return SDM_GX_ERR_PLAN;
@@ -189,23 +203,77 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
     return SDM_GX_OK;
 }
 
-// The planner (rules fitted to interleaved timing sweeps of every plan on MI355X; the choice never changes results).
-// Engine: the matrix cores for chunks with 32 <= C and hd <= 128, where their streaming kernel measured fastest
-// (64x64, 64x128 and 128x128 chunks); the vector-ALU chain otherwise (narrow C, where 64-row MFMA tiles would be
-// mostly padding, and wide hd, where the vector-ALU kernel's direct d_dv reads stream at least as fast).
-//  Matrix cores, when C and the row stride of d_dv are multiples of 4: 16-column wavefronts
-//  (v_mfma_f32_16x16x1_4b_f32: half the chain latency per work item of the 32-column MFMA) with slabs moved straight
-//  to LDS (3 stages, 1 loader wavefront: 1-3% faster than 4 stages; 6 or 8 stages are slower). Work items of 64 or
-//  128 rows (C <= 64 or not) by 64 columns (32 when hd <= 32, or when 64-column items would leave CUs idle; 64 rows
-//  by 128 columns when C > 64 and hd is a multiple of 128, with items enough for every CU); two
-//  workgroups per CU when an item has fewer than 8 compute wavefronts and there are fewer than 4 items per CU, else
-//  one. One workgroup per CU walking several items: stages of 32 chain rows (half the barrier bubbles, which no
-//  other workgroup fills). One item per workgroup: stages of 16 rows (the chain starts on a smaller first slab: 3%
-//  faster on 64x64 chunks at one item per CU). Two workgroups per CU: stages of 16 rows and d_u stores with the
-//  non-temporal hint (6% faster on 64x128 chunks; the hint made 128x128 chunks 6% slower with one workgroup per
-//  CU). Measured against the register-ring instances with launches replayed from graphs: 39% faster on 64x64
-//  chunks, 19% on 64x128, 18% on 128x128. Unaligned rows run the launch-selected unaligned-row twins; strides that
-//  are not multiples of 4 get the register-ring kernel's plan (hd <= 128) or the vector-ALU engine.
+// The matrix-core engine addresses a chunk of d_u with 32-bit byte offsets.
+bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1) << 31); }
+
+// Direct-to-LDS slabs (mf_reg_slabs 0) move 16-byte groups, all rows of x and of d_dv at one offset from a 16-byte
+// boundary (C and ld_dv multiples of 4), and address a chunk of d_dv, and the rows past C that pad its last slab,
+// with 32-bit byte offsets.
+bool dma_strides_ok(int64_t C, int64_t ld_dv) {
+    return C % 4 == 0 && ld_dv % 4 == 0 && (C + 32) * ld_dv * 4 < (int64_t(1) << 31);
+}
+
+// The instance a matrix-core plan runs for a layout. Direct-to-LDS plans whose x or d_dv rows start off a 16-byte
+// boundary take the unaligned-row twin of their instance (mf_aln 4: d_dv rows by 4-byte DMA, x aligned; 2: d_dv rows
+// from the 16-byte boundary below; 3: x rows too). Where the strides rule out direct-to-LDS slabs, or no twin
+// exists, the same work items run through the register ring: 32-column wavefronts (a 16-column tile of 2k column
+// wavefronts is k of them), 2 register slabs, 4 stages, 4 loader wavefronts. The results are the same either way.
+int resolve_layout(sdm_gx_plan_t* p, int64_t C, const Layout& lay) {
+    p->mf_aln = 0;
+    if (p->engine != SDM_GX_ENGINE_MFMA || p->mf_reg_slabs != 0) return SDM_GX_OK;
+    const bool xa = lay.x_mod16 == 0, da = lay.dv_mod16 == 0;
+    if (dma_strides_ok(C, lay.ld_dv)) {
+        if (xa && da) return SDM_GX_OK;
+        for (int aln : {xa ? 4 : 3, xa ? 2 : 3}) {
+            sdm_gx_plan_t q = *p;
+            q.mf_aln = aln;
+            if (find_mfma(q)) {
+                *p = q;
+                return SDM_GX_OK;
+            }
+        }
+    }
+    if (p->mf_block == 16) p->mf_col_waves /= 2;
+    p->mf_block = 32;
+    p->slab_rows = 16;
+    p->mf_stages = 4;
+    p->mf_reg_slabs = 2;
+    p->mf_loader_waves = 4;
+    p->mf_stream_du = 0;        // the register-ring kernel has no streaming-store variant
+    return find_mfma(*p) ? SDM_GX_OK : SDM_GX_ERR_PLAN;
+}
+
+// A plan made complete for a launch: output fields filled, the instance resolved for the layout (mf_aln is an
+// output; its input value is ignored), and every limit the launch will check checked here.
+int finish_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, const Layout& lay, int64_t lds_limit) {
+    p->mf_aln = 0;
+    int st = complete_plan(p, nchunks, C, hd, lds_limit);
+    if (st || p->engine != SDM_GX_ENGINE_MFMA) return st;
+    if (!mfma_strides_ok(C, lay.ld_u)) return SDM_GX_ERR_LIMIT;
+    if ((st = resolve_layout(p, C, lay))) return st;
+    return complete_plan(p, nchunks, C, hd, lds_limit);
+}
+
+// The launch planner. It plays the part of the page's launch rules for gx_gemm (_rows: rows per CTA from the grid
+// target; _cap: CTAs per SM; one_wave: the kernel only for single-wave grids), re-derived for MI355X from
+// interleaved timing of every plan (launches replayed from HIP graphs). The choice never changes results.
+// Engine (`engine` -1): the matrix cores for 32 <= C when the direct-to-LDS kernel can take the strides (C and
+// ld_dv multiples of 4), or when hd <= 128 (register-ring kernel); the vector ALUs otherwise (narrow chunks, where
+// 64-row MFMA tiles would be mostly padding, and wide rows of odd strides). engine 0 or 1 forces one engine; the
+// matrix cores also need C * ld_u * 4 < 2^31 (32-bit d_u offsets), else SDM_GX_ERR_LIMIT when forced.
+//  Matrix cores, direct-to-LDS slabs: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per
+//  work item of the 32-column MFMA), 3 LDS stages, 1 loader wavefront (1-3% faster than 4 stages; 6 or 8 slower).
+//  Work items of 64 or 128 rows (C <= 64 or not) by 64 columns; 32 columns when hd <= 32, or when 64-column items
+//  would leave CUs idle; 64 rows by 128 columns when C > 64 and hd is a multiple of 128 with items enough for every
+//  CU (2% faster than 128 x 64 at C = hd = 128). Two workgroups per CU when an item has fewer than 8 compute
+//  wavefronts and there are fewer than 4 items per CU, else one. One workgroup per CU walking several items: stages
+//  of 32 chain rows (half the barrier bubbles, which no other workgroup fills). One item per workgroup: stages of 16
+//  rows (the chain starts on a smaller first slab). Two workgroups per CU: stages of 16 rows and d_u stores with the
+//  non-temporal hint (6% faster on 64x128 chunks; 6% slower on 128x128 chunks with one workgroup per CU). Rows off a
+//  16-byte boundary take the unaligned-row twins (resolve_layout).
+//  Matrix cores, register ring (strides that rule out direct-to-LDS slabs, hd <= 128): 32-column wavefronts, 64 or
+//  128 rows by up to 128 columns, 4 register slabs and 4 stages; 128 x 128 items with 2 register slabs, d_u read at
+//  the item's end and two workgroups per CU.
 //  Vector ALUs:
 //  * Columns per lane RC: the widest RC whose 64*RC-column blocks waste no more lanes than a narrower one.
 //  * Rows per wavefront RI: 8 (two batches of 4 rows of x in flight), halved to 4 while the grid would
@@ -216,14 +284,16 @@ int complete_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, int6
 //  * RC <= 2: the workgroup stages d_dv through a 32 KiB LDS slab, with the XCD-grouped workgroup order.
 //    RC = 4: each wavefront reads d_dv straight from global memory (64 columns of 16 bytes per row: the LDS round
 //    trip measured slower there).
-// allow_mfma = false forces the vector-ALU engine (row strides too large for the matrix-core engine's 32-bit
-// buffer offsets).
-int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit, sdm_gx_plan_t* out,
-             bool allow_mfma, bool dma_ok) {
+int plan_for(int64_t nchunks, int64_t C, int64_t hd, const Layout& lay, int engine, int num_cus, int lds_limit,
+             sdm_gx_plan_t* out) {
     if (!out) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT || nchunks < 0) return SDM_GX_ERR_SHAPE;
+    if (engine != -1 && engine != SDM_GX_ENGINE_VALU && engine != SDM_GX_ENGINE_MFMA) return SDM_GX_ERR_ARG;
     if (num_cus < 1) num_cus = kDefaultCus;
-    if (allow_mfma && C >= 32 && (dma_ok || hd <= 128)) {
+    const bool allow_mfma = engine != SDM_GX_ENGINE_VALU && mfma_strides_ok(C, lay.ld_u);
+    if (engine == SDM_GX_ENGINE_MFMA && !allow_mfma) return SDM_GX_ERR_LIMIT;
+    const bool dma_ok = dma_strides_ok(C, lay.ld_dv);
+    if (allow_mfma && (engine == SDM_GX_ENGINE_MFMA || (C >= 32 && (dma_ok || hd <= 128)))) {
         sdm_gx_plan_t p{};
         p.engine = SDM_GX_ENGINE_MFMA;
         int st;
@@ -233,7 +303,7 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             p.mf_col_waves = hd > 32 ? 4 : 2;
             if (nchunks * cdiv(C, 64 * p.mf_row_waves) * cdiv(hd, 64) < num_cus) p.mf_col_waves = 2;
             else if (C > 64 && hd % 128 == 0 && nchunks * cdiv(C, 64) * (hd / 128) >= num_cus) {
-                p.mf_row_waves = 1;                     // 64 x 128 items: 2% faster than 128 x 64 at C = hd = 128
+                p.mf_row_waves = 1;                     // 64 x 128 items
                 p.mf_col_waves = 8;
             }
             p.mf_stages = 3;
@@ -244,10 +314,7 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
             p.slab_rows = 16;
             st = complete_plan(&p, nchunks, C, hd, lds_limit);
             if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU
-                if (items > p.grid) {                           // walking several items: 32-row stages
-                    p.slab_rows = 32;
-                    st = complete_plan(&p, nchunks, C, hd, lds_limit);
-                }
+                if (items > p.grid) p.slab_rows = 32;           // walking several items: 32-row stages
             } else {                                            // two per CU: streaming d_u stores
                 p.mf_stream_du = 1;
             }
@@ -264,13 +331,13 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
                 p.mf_du_at_end = 1;
                 p.mf_workgroups = 2 * num_cus;
             }
-            st = complete_plan(&p, nchunks, C, hd, lds_limit);
         }
+        st = finish_plan(&p, nchunks, C, hd, lay, lds_limit);
         if (st == SDM_GX_OK) {
             *out = p;
             return SDM_GX_OK;
         }
-        if (st != SDM_GX_ERR_LIMIT) return st;
+        if (st != SDM_GX_ERR_LIMIT || engine == SDM_GX_ENGINE_MFMA) return st;
     }
     int rc = 1;
     int64_t best_waste = cdiv(hd, 64) * 64 - hd;
@@ -297,28 +364,18 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, int num_cus, int lds_limit,
     p.staging = rc <= 2 ? 1 : 0;
     p.xcd_remap = rc <= 2 ? 1 : 0;
     p.slab_rows = 0;
-    int st = complete_plan(&p, nchunks, C, hd, lds_limit);
+    int st = finish_plan(&p, nchunks, C, hd, lay, lds_limit);
     if (st == SDM_GX_ERR_LIMIT) {               // a device with less LDS per workgroup: read d_dv directly
         p.staging = 0;
-        st = complete_plan(&p, nchunks, C, hd, lds_limit);
+        st = finish_plan(&p, nchunks, C, hd, lay, lds_limit);
     }
     if (st) return st;
     *out = p;
     return SDM_GX_OK;
 }
 
-// The matrix-core engine addresses a chunk of d_u with 32-bit byte offsets.
-bool mfma_strides_ok(int64_t C, int64_t ld_u) { return C * ld_u * 4 < (int64_t(1) << 31); }
-
-// Direct-to-LDS slabs (mf_reg_slabs 0) move 16-byte groups, all rows of x and of d_dv at one offset from a 16-byte
-// boundary (C and ld_dv multiples of 4), and address a chunk of d_dv, and the rows past C that pad its last slab,
-// with 32-bit byte offsets.
-bool dma_strides_ok(int64_t C, int64_t ld_dv) {
-    return C % 4 == 0 && ld_dv % 4 == 0 && (C + 32) * ld_dv * 4 < (int64_t(1) << 31);
-}
-bool rows_aligned16(const float* x, const float* dv) {
-    return reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0;
-}
+// The placement arguments of the planner entry points: byte offsets from a 16-byte boundary.
+bool valid_mod16(int32_t v) { return v >= 0 && v < 16 && v % 4 == 0; }
 
 // ---- launching ----------------------------------------------------------------------------------------------------
 // Chunks n_begin .. n_begin + nchunks - 1 with a completed, validated plan. Splits very large grids so that one
@@ -345,34 +402,15 @@ int for_each_launch(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float
         const sdm_gx::MfmaEntry* e = find_mfma(p);
         if (!e) return SDM_GX_ERR_PLAN;
         if (!mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
-        sdm_gx_plan_t q = p;
         if (e->reg_slabs == 0) {
-            const sdm_gx::MfmaEntry* twin = nullptr;
-            if (dma_strides_ok(C, ld_dv) && !rows_aligned16(x, dv)) {    // rows off a 16-byte boundary
-                // x aligned: d_dv rows by 4-byte DMA (4), else from the 16-byte boundary below (2); x too: 3
-                const bool xa = reinterpret_cast<uintptr_t>(x) % 16 == 0;
-                for (int aln : {xa ? 4 : 3, xa ? 2 : 3}) {
-                    twin = sdm_gx::find_mfma_kernel(e->row_waves, e->col_waves, e->stages, 0, e->loader_waves,
-                                                    e->du_at_end, e->block, e->slab_rows, aln);
-                    if (twin) break;
-                }
-            }
-            if (twin) {
-                e = twin;
-            } else if (!dma_strides_ok(C, ld_dv) || !rows_aligned16(x, dv)) {
-                // slabs cannot go straight to LDS: the same work items through the register ring (32-column
-                // wavefronts: a mf_block 16 tile of 2k column wavefronts is k of them)
-                if (e->block == 16) q.mf_col_waves = e->col_waves / 2;
-                q.mf_block = 32;
-                q.slab_rows = 16;
-                q.mf_stages = 4;
-                q.mf_reg_slabs = 2;
-                q.mf_loader_waves = 4;
-                e = find_mfma(q);
-                if (!e) return SDM_GX_ERR_PLAN;
-            }
+            // the plan was resolved for this layout (finish_plan); a direct-to-LDS instance needs its strides, and
+            // rows on 16-byte boundaries wherever it has no unaligned-row path for them
+            const Layout lay = layout_of(ld_u, ld_dv, x, dv);
+            if (!dma_strides_ok(C, ld_dv) || (!(e->aln & 1) && lay.x_mod16 != 0) ||
+                (!(e->aln & 6) && lay.dv_mod16 != 0))
+                return SDM_GX_ERR_PLAN;
         }
-        const MfmaGeom g = mfma_geom(q, nchunks, C, hd);
+        const MfmaGeom g = mfma_geom(p, nchunks, C, hd);
         if (g.items >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;     // item indices are 32-bit in the kernel
         r.mfma = true;
         r.fn = e->fn;
@@ -438,19 +476,15 @@ int launch_chunks(const sdm_gx_plan_t& p, float* du, int64_t ld_u, const float* 
     });
 }
 
-// Plan (given or planned) for nchunks chunks on a device with `info`; ld_u: the row stride the launch will use.
-int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv,
+// Plan (given or planned) for nchunks chunks on a device with `info`, resolved for the launch's layout.
+int resolve_plan(const sdm_gx_plan_t* given, int64_t nchunks, int64_t C, int64_t hd, const Layout& lay,
                  const DeviceInfo& info, sdm_gx_plan_t* out) {
     if (given) {
         *out = *given;
         if (out->engine == SDM_GX_ENGINE_MFMA && out->mf_workgroups == 0) out->mf_workgroups = info.num_cus;
-        const int st = complete_plan(out, nchunks, C, hd, info.lds_per_wg);
-        if (st) return st;
-        if (out->engine == SDM_GX_ENGINE_MFMA && !mfma_strides_ok(C, ld_u)) return SDM_GX_ERR_LIMIT;
-        return SDM_GX_OK;
+        return finish_plan(out, nchunks, C, hd, lay, info.lds_per_wg);
     }
-    return plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, mfma_strides_ok(C, ld_u),
-                    dma_strides_ok(C, ld_dv));
+    return plan_for(nchunks, C, hd, lay, -1, info.num_cus, info.lds_per_wg, out);
 }
 
 int check_device_pointers(const float* du, const float* x, const float* dv, int dev) {
@@ -478,7 +512,7 @@ int sdm_gx_gemm_ex(float* d_u, int64_t ld_u, const float* x, const float* d_dv, 
     if ((st = current_device(&dev, &info))) return st;
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_plan_t p;
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, layout_of(ld_u, ld_dv, x, d_dv), info, &p))) return st;
     return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, static_cast<hipStream_t>(stream));
 }
 
@@ -508,10 +542,10 @@ int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_d
     sdm_gx_plan_t p;
     if (mode == SDM_GX_STEPS_FUSED) {
         const int64_t nchunks = (ti_end - ti_begin) * P;
-        if ((st = resolve_plan(plan, nchunks, C, hd, ld_u, ld_dv, info, &p))) return st;
+        if ((st = resolve_plan(plan, nchunks, C, hd, layout_of(ld_u, ld_dv, x, d_dv), info, &p))) return st;
         return launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti_begin * P, nchunks, C, hd, s);
     }
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &p))) return st;
+    if ((st = resolve_plan(plan, P, C, hd, layout_of(ld_u, ld_dv, x, d_dv), info, &p))) return st;
     for (int64_t k = 0; k < ti_end - ti_begin; ++k) {
         const int64_t ti = mode == SDM_GX_STEPS_FORWARD ? ti_begin + k : ti_end - 1 - k;
         if ((st = launch_chunks(p, d_u, ld_u, x, d_dv, ld_dv, ti * P, P, C, hd, s))) return st;
@@ -519,8 +553,11 @@ int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const float* d_d
     return SDM_GX_OK;
 }
 
-int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_plan_t* out) {
+int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv, int32_t x_mod16,
+                int32_t dv_mod16, int32_t engine, int32_t device, sdm_gx_plan_t* out) {
     if (!out) return SDM_GX_ERR_ARG;
+    if (ld_u < hd || ld_dv < hd || ld_u >= SDM_GX_LD_LIMIT || ld_dv >= SDM_GX_LD_LIMIT) return SDM_GX_ERR_STRIDE;
+    if (!valid_mod16(x_mod16) || !valid_mod16(dv_mod16)) return SDM_GX_ERR_ALIGN;
     int dev = device;
     if (dev < 0) {
         hipError_t e = hipGetDevice(&dev);
@@ -530,7 +567,8 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
     int st = device_info(dev, &info);
     if (st) return st;
     if (!info.gfx950) return SDM_GX_ERR_DEVICE;
-    if ((st = plan_for(nchunks, C, hd, info.num_cus, info.lds_per_wg, out, true, dma_strides_ok(C, hd)))) return st;
+    const Layout lay{ld_u, ld_dv, x_mod16, dv_mod16};
+    if ((st = plan_for(nchunks, C, hd, lay, engine, info.num_cus, info.lds_per_wg, out))) return st;
     const void* fn;
     int threads, dyn_lds;
     if (out->engine == SDM_GX_ENGINE_MFMA) {
@@ -551,15 +589,21 @@ int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_p
     return SDM_GX_OK;
 }
 
-int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int32_t num_cus, int32_t lds_per_cu,
-                    sdm_gx_plan_t* out) {
-    return plan_for(nchunks, C, hd, num_cus, lds_per_cu, out, true, dma_strides_ok(C, hd));
+int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv, int32_t x_mod16,
+                    int32_t dv_mod16, int32_t engine, int32_t num_cus, int32_t lds_per_cu, sdm_gx_plan_t* out) {
+    if (!out) return SDM_GX_ERR_ARG;
+    if (ld_u < hd || ld_dv < hd || ld_u >= SDM_GX_LD_LIMIT || ld_dv >= SDM_GX_LD_LIMIT) return SDM_GX_ERR_STRIDE;
+    if (!valid_mod16(x_mod16) || !valid_mod16(dv_mod16)) return SDM_GX_ERR_ALIGN;
+    return plan_for(nchunks, C, hd, Layout{ld_u, ld_dv, x_mod16, dv_mod16}, engine, num_cus, lds_per_cu, out);
 }
 
-int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd, int32_t lds_per_cu) {
+int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv,
+                         int32_t x_mod16, int32_t dv_mod16, int32_t lds_per_cu) {
     if (!plan) return SDM_GX_ERR_ARG;
     if (C < 1 || C > SDM_GX_MAX_C || hd < 1 || hd >= SDM_GX_HD_LIMIT) return SDM_GX_ERR_SHAPE;
-    return complete_plan(plan, nchunks, C, hd, lds_per_cu);
+    if (ld_u < hd || ld_dv < hd || ld_u >= SDM_GX_LD_LIMIT || ld_dv >= SDM_GX_LD_LIMIT) return SDM_GX_ERR_STRIDE;
+    if (!valid_mod16(x_mod16) || !valid_mod16(dv_mod16)) return SDM_GX_ERR_ALIGN;
+    return finish_plan(plan, nchunks, C, hd, Layout{ld_u, ld_dv, x_mod16, dv_mod16}, lds_per_cu);
 }
 
 int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
@@ -574,8 +618,9 @@ int sdm_gx_prepare(sdm_gx_launch_t* out, float* d_u, int64_t ld_u, const float* 
     if ((st = check_device_pointers(d_u, x, d_dv, dev))) return st;
     sdm_gx_launch_t l;
     std::memset(&l, 0, sizeof(l));
-    if ((st = resolve_plan(plan, P, C, hd, ld_u, ld_dv, info, &l.plan_step))) return st;
-    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, ld_u, ld_dv, info, &l.plan_fused))) return st;
+    const Layout lay = layout_of(ld_u, ld_dv, x, d_dv);
+    if ((st = resolve_plan(plan, P, C, hd, lay, info, &l.plan_step))) return st;
+    if ((st = resolve_plan(plan, (ti_max + 1) * P, C, hd, lay, info, &l.plan_fused))) return st;
     l.device = dev;
     l.d_u = d_u;
     l.x = x;

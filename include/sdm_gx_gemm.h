@@ -20,9 +20,16 @@
  *   x     [N][C][C]               x[n, j, i]    at (n*C + j)*C + i        (contiguous; used transposed)
  *   d_dv  [N][C] rows of ld_dv    d_dv[n, j, c] at (n*C + j)*ld_dv + c    (c < hd <= ld_dv)
  *   d_u   [N][C] rows of ld_u     d_u[n, i, c]  at (n*C + i)*ld_u + c     (c < hd <= ld_u), updated in place
- * Only columns c < hd of the chunks of the requested steps are read (d_dv, d_u) or written (d_u); x is read for
- * those chunks only. The library never touches memory past element (N*C - 1)*ld + hd - 1 of d_u / d_dv, nor the
- * padding columns hd..ld-1 of any row. Chunks n >= (N / P) * P belong to no step and are never touched.
+ * Writes: only d_u[n, i, c] with c < hd, for the chunks n of the requested steps; padding columns hd..ld_u-1 and
+ * every other chunk keep their bytes.
+ * Reads: d_u only where it is written. x and d_dv only inside the chunks of the requested steps, where the
+ * matrix-core engine's direct-to-LDS kernel moves whole 16-byte groups: it may read any element of such a chunk of
+ * x, and the elements of such a chunk of d_dv from its first row start through element (C-1)*ld_dv + hd - 1 (so the
+ * padding columns of every row but the chunk's last); when x or d_dv starts off a 16-byte boundary it may also read
+ * the bytes from the 16-byte boundary at or below each row start (the same 16-byte block, hence the same page, as the
+ * row's first element; for the first row of chunk 0 that is up to 12 bytes below the pointer passed in). No value
+ * read outside columns c < hd reaches a result. The other kernels read only columns c < hd. Chunks
+ * n >= (N / P) * P belong to no step and are never touched.
  *
  * Ownership and execution: every pointer is caller-owned device memory of the current HIP device (for example a
  * torch tensor's data_ptr()). The library allocates nothing on the caller's behalf, keeps no pointer after a call
@@ -44,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SDM_GX_ABI_VERSION 3
+#define SDM_GX_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define SDM_GX_API __attribute__((visibility("default")))
@@ -102,10 +109,11 @@ typedef enum sdm_gx_status {
  *                    mf_reg_slabs 0: 4 or 8 for mf_block 32, 3 or 8 for mf_block 16)
  *   mf_reg_slabs     slabs of 16 chain rows the loader wavefronts keep in flight in registers (2 or 4), or 0: the
  *                    loader wavefronts move slabs straight from memory into the LDS ring (buffer loads to LDS), up
- *                    to mf_stages - 1 slabs in flight. That needs x and d_dv rows on 16-byte boundaries (x and d_dv
- *                    16-byte aligned, C and ld_dv multiples of 4, C * ld_dv * 4 < 2^31); a launch whose pointers or
- *                    strides do not allow it runs the same tiles through the register ring (2 register slabs,
- *                    4 stages, 4 loader wavefronts), with the same results
+ *                    to mf_stages - 1 slabs in flight. That needs C and ld_dv multiples of 4 and
+ *                    (C + 32) * ld_dv * 4 < 2^31; rows off a 16-byte boundary run an unaligned-row instance
+ *                    (mf_aln). Completing a plan for a layout that rules it out gives the register-ring plan of the
+ *                    same work items (32-column wavefronts, 2 register slabs, 4 stages, 4 loader wavefronts), with
+ *                    the same results
  *   mf_loader_waves  loader wavefronts per workgroup (2 or 4 with register slabs, 4 with 4 register slabs for 64x256
  *                    and 128x128 items; with mf_reg_slabs 0: 1 with 4 stages, 2 with 8 stages)
  *   mf_workgroups    workgroups to launch (0: one per compute unit); each takes a contiguous range of work items
@@ -122,9 +130,16 @@ typedef enum sdm_gx_status {
  *                    wavefronts (mf_col_waves 2 -> 1 ..), register slabs as above
  *   mf_stream_du     mf_reg_slabs 0: 1 = d_u stores carry the non-temporal (streaming) cache hint; 0 = plain stores.
  *                    No effect on results.
- * Outputs of the planner / sdm_gx_plan_complete:
+ * Outputs of the planner / sdm_gx_plan_complete (also filled in the plans of a prepared launch, for the layout of
+ * its pointers and strides; input values are ignored):
  *   lds_bytes      LDS bytes per workgroup (dynamic for the VALU engine, static for the MFMA engine)
  *   wgs_per_cu     workgroups per CU that can be resident (0 if not known)
+ *   mf_aln         which instance a direct-to-LDS plan (mf_reg_slabs 0) runs for rows that start off a 16-byte
+ *                  boundary: 0 rows on 16-byte boundaries; 4 d_dv rows moved by 4-byte DMA (x aligned); 2 d_dv rows
+ *                  loaded from the 16-byte boundary below each row start (x aligned); 3 x and d_dv rows both so.
+ *                  A direct-to-LDS plan whose layout has no such instance (or whose strides rule out direct-to-LDS
+ *                  slabs) is completed as the register-ring plan that runs the same work items, as described under
+ *                  mf_reg_slabs; the plan reported is the kernel that runs
  *   grid           workgroups for the chunk count it was planned for */
 typedef struct sdm_gx_plan {
     int32_t engine;
@@ -145,6 +160,7 @@ typedef struct sdm_gx_plan {
     int32_t mf_du_at_end;
     int32_t mf_block;
     int32_t mf_stream_du;
+    int32_t mf_aln;
     int64_t grid;
 } sdm_gx_plan_t;
 
@@ -180,16 +196,32 @@ SDM_GX_API int sdm_gx_gemm_steps(float* d_u, int64_t ld_u, const float* x, const
 SDM_GX_API int sdm_gx_check(const float* d_u, int64_t ld_u, const float* x, const float* d_dv, int64_t ld_dv,
                             int64_t N, int64_t ti, int64_t P, int64_t C, int64_t hd);
 
-/* The planner for `nchunks` chunks of shape (C, hd) on HIP device `device` (-1: current device). Fills *out. */
-SDM_GX_API int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int32_t device, sdm_gx_plan_t* out);
+/* The launch planner: the plan a launch over `nchunks` chunks of shape (C, hd) runs, on HIP device `device` (-1: the
+ * current device). It takes the part of the page's launch rules for gx_gemm (_rows: rows per CTA from a grid target;
+ * _cap: CTAs per SM, forced by padding shared memory; one_wave: the kernel only when its grid fits one wave),
+ * re-derived for MI355X: engine, work-item tile, LDS stages and workgroups per CU, for single- and multi-wave grids
+ * alike. The result never changes the output bits.
+ *   ld_u, ld_dv        the row strides the launch will use (hd <= ld < 2^31; else SDM_GX_ERR_STRIDE)
+ *   x_mod16, dv_mod16  the byte offsets of x and d_dv from a 16-byte boundary (address mod 16: 0, 4, 8 or 12; else
+ *                      SDM_GX_ERR_ALIGN); with the strides they decide which kernel instance runs (mf_aln)
+ *   engine             -1: the planner's choice; SDM_GX_ENGINE_VALU or SDM_GX_ENGINE_MFMA: that engine
+ *                      (SDM_GX_ERR_LIMIT when the matrix-core engine cannot take the strides)
+ * The plan filled in is exactly what sdm_gx_gemm_ex / sdm_gx_gemm_steps / sdm_gx_prepare run for those arguments
+ * when given no plan (engine -1). */
+SDM_GX_API int sdm_gx_plan(int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv, int32_t x_mod16,
+                           int32_t dv_mod16, int32_t engine, int32_t device, sdm_gx_plan_t* out);
 
-/* The same planner with the device facts given explicitly (no HIP call): compute units and LDS bytes per CU. */
-SDM_GX_API int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int32_t num_cus, int32_t lds_per_cu,
-                               sdm_gx_plan_t* out);
+/* The same planner with the device facts given explicitly (no HIP call): compute units and LDS bytes per
+ * workgroup. */
+SDM_GX_API int sdm_gx_plan_for(int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u, int64_t ld_dv,
+                               int32_t x_mod16, int32_t dv_mod16, int32_t engine, int32_t num_cus,
+                               int32_t lds_per_cu, sdm_gx_plan_t* out);
 
-/* Validate a caller-made plan for shape (C, hd) and fill its output fields for `nchunks` chunks. */
-SDM_GX_API int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd,
-                                    int32_t lds_per_cu);
+/* Validate a caller-made plan for shape (C, hd), strides and placement as for sdm_gx_plan, and fill its output
+ * fields for `nchunks` chunks (the page's gx_gemm checks its ti_rows argument the same way: a plan that does not fit
+ * is an error, never silently replaced). */
+SDM_GX_API int sdm_gx_plan_complete(sdm_gx_plan_t* plan, int64_t nchunks, int64_t C, int64_t hd, int64_t ld_u,
+                                    int64_t ld_dv, int32_t x_mod16, int32_t dv_mod16, int32_t lds_per_cu);
 
 /* A prepared step launch (the page's GemmPlan): everything is validated once for every ti <= ti_max, then
  * sdm_gx_launch issues step ti with only ti changed. The struct is caller-owned plain data; it holds the three

@@ -41,7 +41,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_abi_version():
-    assert g.sdm_gx_abi_version() == 3
+    assert g.sdm_gx_abi_version() == 4
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -51,12 +51,12 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "sdm_gx_gemm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sdm_gx_plan_t), offsetof(sdm_gx_plan_t, grid),
          sizeof(sdm_gx_launch_t), offsetof(sdm_gx_launch_t, ti_max), offsetof(sdm_gx_launch_t, plan_step),
          offsetof(sdm_gx_launch_t, plan_fused), offsetof(sdm_gx_plan_t, slab_rows),
          offsetof(sdm_gx_plan_t, mf_row_waves), offsetof(sdm_gx_plan_t, mf_workgroups),
          offsetof(sdm_gx_plan_t, mf_du_at_end), offsetof(sdm_gx_plan_t, mf_block),
-         offsetof(sdm_gx_plan_t, mf_stream_du));
+         offsetof(sdm_gx_plan_t, mf_stream_du), offsetof(sdm_gx_plan_t, mf_aln));
   return 0;
 }
 """)
@@ -68,7 +68,7 @@ int main(void) {
                     g.sdm_gx_launch_t.plan_fused.offset, g.sdm_gx_plan_t.slab_rows.offset,
                     g.sdm_gx_plan_t.mf_row_waves.offset, g.sdm_gx_plan_t.mf_workgroups.offset,
                     g.sdm_gx_plan_t.mf_du_at_end.offset, g.sdm_gx_plan_t.mf_block.offset,
-                    g.sdm_gx_plan_t.mf_stream_du.offset]
+                    g.sdm_gx_plan_t.mf_stream_du.offset, g.sdm_gx_plan_t.mf_aln.offset]
 
 
 def test_strerror_covers_every_code():
@@ -147,6 +147,7 @@ def test_plan_for_emits_supported_plans():
     for nchunks in (0, 1, 7, 128, 4096):
         for C, hd in shapes:
             p = g.sdm_gx_plan_for(nchunks, C, hd)
+            assert p.mf_aln == 0                       # rows on 16-byte boundaries (ld = hd, aligned bases)
             # engine rule: matrix cores for 32 <= C when slabs can go straight to LDS (C and the row stride, taken
             # as hd here, multiples of 4), or for hd <= 128 through the register ring
             assert p.engine == (g.SDM_GX_ENGINE_MFMA if C >= 32 and (dma_ok(C, hd) or hd <= 128)
@@ -238,11 +239,16 @@ MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs
 @pytest.mark.parametrize("rw,cw,s,rs,lw,de,blk,j", MFMA_INSTANCES)
 def test_mfma_plan_complete_geometry(rw, cw, s, rs, lw, de, blk, j):
     for nchunks, C, hd, wgs in ((512, 128, 128, 0), (7, 200, 33, 3), (1, 1, 1, 0), (1000, 64, 256, 100), (0, 64, 64, 0)):
-        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, wgs, de, blk, j), nchunks, C, hd)
-        items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, blk * cw)
+        ld = cdiv(hd, 4) * 4                    # a stride direct-to-LDS slabs can take
+        p = g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, wgs, de, blk, j), nchunks, C, hd,
+                                   ld_u=ld, ld_dv=ld)
+        ers, es, ej, eblk, ecw = rs, s, j, blk, cw
+        if rs == 0 and not dma_ok(C, ld):       # C not a multiple of 4: the register-ring form of the plan
+            ers, es, ej, eblk, ecw = 2, 4, 16, 32, (cw // 2 if blk == 16 else cw)
+        items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, eblk * ecw)
         assert p.grid == mfma_grid(items, wgs or 256)
-        assert p.lds_bytes == 16 * s * j * (16 * rw + blk // 4 * cw)
-        assert p.mf_block == blk and p.slab_rows == j
+        assert p.lds_bytes == 16 * es * ej * (16 * rw + eblk // 4 * ecw)
+        assert (p.mf_block, p.slab_rows, p.mf_reg_slabs, p.mf_col_waves) == (eblk, ej, ers, ecw)
 
 
 def test_mfma_block_zero_means_32():
@@ -271,6 +277,61 @@ def test_mfma_direct_to_lds_rejects_missing_instances():
                                       (1, 2, 3, 0, 1, 32, 16)):
         with pytest.raises(ValueError):
             g.sdm_gx_plan_complete(g.make_mfma_plan(rw, cw, s, rs, lw, 0, 0, blk, j), 4, 64, 64)
+
+def test_plan_resolves_the_layout():
+    """The planner takes the row strides and the placement of x and d_dv, and reports the instance that a launch with
+    that layout runs (unaligned-row twins, or the register ring where the strides rule out direct-to-LDS slabs)."""
+    # workload 5's layout: ld 260, d_u and d_dv at +4 bytes, x aligned: d_dv rows by 4-byte DMA
+    p = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=0, dv_mod16=4)
+    assert (p.engine, p.mf_reg_slabs, p.mf_block, p.mf_aln) == (g.SDM_GX_ENGINE_MFMA, 0, 16, 4)
+    assert p.lds_bytes == 16 * 3 * p.slab_rows * 16 + 4 * 3 * p.slab_rows * 16 * p.mf_col_waves
+    # x off the boundary too: both from the 16-byte boundary below (one more group per LDS row)
+    q = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=8, dv_mod16=4)
+    assert (q.mf_reg_slabs, q.mf_aln) == (0, 3) and q.lds_bytes > p.lds_bytes
+    # 64 x 128 items with 32-row stages have no 4-byte-DMA twin: from the boundary below
+    r = g.sdm_gx_plan_for(512, 128, 128, x_mod16=0, dv_mod16=12)
+    assert (r.mf_row_waves, r.mf_col_waves, r.slab_rows, r.mf_aln) == (1, 8, 32, 2)
+    # a row stride that is not a multiple of 4: the register ring (hd <= 128), or the vector ALUs (hd > 128)
+    s_ = g.sdm_gx_plan_for(256, 64, 128, ld_u=131, ld_dv=131)
+    assert (s_.engine, s_.mf_reg_slabs, s_.mf_block, s_.mf_aln) == (g.SDM_GX_ENGINE_MFMA, 4, 32, 0)
+    assert g.sdm_gx_plan_for(256, 64, 200, ld_u=203, ld_dv=203).engine == g.SDM_GX_ENGINE_VALU
+    # d_u's stride alone never changes the instance, unless the 32-bit d_u offsets would overflow
+    assert g.sdm_gx_plan_for(256, 64, 128, ld_u=131, ld_dv=128).mf_reg_slabs == 0
+    assert g.sdm_gx_plan_for(2, 256, 64, ld_u=1 << 21, ld_dv=64).engine == g.SDM_GX_ENGINE_VALU
+
+
+def test_plan_complete_resolves_the_layout():
+    """A caller-made direct-to-LDS plan is completed for the layout: its unaligned-row twin, or the register-ring plan
+    of the same work items where there is none; mf_aln on input is ignored."""
+    p = g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 16)
+    p.mf_aln = 3
+    assert g.sdm_gx_plan_complete(p, 64, 64, 128).mf_aln == 0
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 16), 64, 64, 128, dv_mod16=8)
+    assert (p.mf_reg_slabs, p.mf_aln, p.mf_col_waves) == (0, 4, 4)
+    # 32-column direct-to-LDS instances have no twins: the register ring, same tile
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 2, 4, 0, 1, 0, 0, 32, 16), 64, 64, 128, x_mod16=4)
+    assert (p.mf_reg_slabs, p.mf_stages, p.mf_loader_waves, p.mf_block, p.mf_col_waves, p.mf_aln) == \
+        (2, 4, 4, 32, 2, 0)
+    # 16-column plan, odd stride: the register ring with half the column wavefronts (32 columns each)
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 32, 1), 64, 64, 128, ld_u=130, ld_dv=130)
+    assert (p.mf_reg_slabs, p.mf_block, p.mf_col_waves, p.slab_rows, p.mf_stream_du) == (2, 32, 2, 16, 0)
+
+
+@pytest.mark.parametrize("kw", [dict(x_mod16=2), dict(dv_mod16=16), dict(x_mod16=-4), dict(ld_u=63),
+                                dict(ld_dv=1 << 31), dict(engine=2), dict(engine=-2)])
+def test_planner_rejects_bad_layout_arguments(kw):
+    with pytest.raises(ValueError):
+        g.sdm_gx_plan_for(8, 64, 64, **kw)
+
+
+def test_planner_engine_choice():
+    assert g.sdm_gx_plan_for(128, 64, 64, engine=g.SDM_GX_ENGINE_VALU).engine == g.SDM_GX_ENGINE_VALU
+    assert g.sdm_gx_plan_for(2, 16, 16).engine == g.SDM_GX_ENGINE_VALU
+    p = g.sdm_gx_plan_for(2, 16, 16, engine=g.SDM_GX_ENGINE_MFMA)
+    assert p.engine == g.SDM_GX_ENGINE_MFMA and p.mf_reg_slabs == 0
+    with pytest.raises(RuntimeError):           # 32-bit d_u offsets: the matrix cores cannot take this stride
+        g.sdm_gx_plan_for(2, 256, 64, ld_u=1 << 21, engine=g.SDM_GX_ENGINE_MFMA)
+
 
 def test_plan_complete_rows_beyond_c():
     with pytest.raises(ValueError):

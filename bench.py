@@ -1,11 +1,24 @@
 """Benchmark of the deterministic FP32 per-step d_u update on one MI355X.
 
-One benchmark step is one pass of the whole hot path over the workload: the prepared multi-step driver running all T
-steps of the workload (by default as one fused launch; --driver per-step issues one launch per step). Inputs are
-synthetic, seeded and resident in device memory before timing starts. Prints ONE JSON line.
+One benchmark step is one pass of the whole hot path over one workload: the prepared multi-step driver running all
+T gx_gemm steps of the workload (by default as one fused launch; --driver per-step issues one launch per step). The
+headline workload is workload 5 (T=2 x P=512 chunks, C=64, hd=256, row stride 260, d_u and d_dv bases at +4 B), the
+largest of the five. Inputs are synthetic, seeded and resident in device memory before any timing starts. Prints ONE
+JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--driver fused|per-step|graph] [--cold]
-                  [--plan ...] [--no-cpu] [--cpu-seconds S]
+What the line holds:
+  value / ms_per_step / roofline   the headline workload, warm: K passes back to back on one stream between two
+                                   HIP events (the figure a kernel trace of back-to-back launches averages to)
+  cold                             the same pass with every cache flushed first: batches of (read 1 GiB, pass)
+                                   minus batches of (read 1 GiB), per pass; d_u's write-back is charged to the pass
+  per_step_driver                  the same pass as T launches, one per gx_gemm step
+  workloads                        workloads 2-5: both engines warm, the default engine cold and per step, each
+                                   pass checked bit for bit against the CPU oracle; and a device copy of the same
+                                   bytes (half read, half written) warm and cold, as a streaming yardstick
+  cpu_baseline                     the CPU oracle, unchanged, on this host's cores (and on one core)
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--driver fused|per-step|graph]
+                  [--plan ...] [--only] [--no-cpu] [--cpu-seconds S] [--profile warm|cold]
 """
 
 from __future__ import annotations
@@ -28,6 +41,7 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
 VALU_FP32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 METRIC = "GFLOP/s and HBM GB/s per gx_gemm step (fraction of roofline), bit-exact"
 KERNEL_SOURCES = ("deterministic_fp32_gemm_amd/csrc/gx_gemm_kernel.hip", "deterministic_fp32_gemm_amd/csrc/gx_gemm_mfma.hip")
+FLUSH_BYTES = 1 << 30               # larger than the 256 MB Infinity Cache and the 8 x 4 MB of L2
 
 
 def kernel_hash() -> str:
@@ -43,7 +57,7 @@ def kernel_hash() -> str:
 
 PLAN_KEYS = ("engine", "rows_per_wave", "cols_per_lane", "waves_per_wg", "staging", "xcd_remap", "slab_rows",
              "mf_row_waves", "mf_col_waves", "mf_stages", "mf_reg_slabs", "mf_loader_waves", "mf_workgroups",
-             "mf_du_at_end", "mf_block", "mf_stream_du")
+             "mf_du_at_end", "mf_block", "mf_stream_du", "mf_aln")
 
 
 def kernel_name(plan: dict) -> str:
@@ -53,8 +67,9 @@ def kernel_name(plan: dict) -> str:
 
 
 def measured_traffic(workload_key: int, driver: str, plan: dict):
-    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled as the
-    copy calibration in profiles/ states), or None unless it was taken on the current kernel source and plan."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE of cold-cache
+    launches, scaled as the copy calibration in profiles/ states), or None unless it was taken on the current kernel
+    source and plan."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name(plan)}_workload{workload_key}_{driver}.json")
     if not os.path.exists(path):
         return None
@@ -67,189 +82,347 @@ def measured_traffic(workload_key: int, driver: str, plan: dict):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cpus():
+    """(CPUs this process may run on: the affinity set within the cgroup's CPU quota, affinity count, quota or None,
+    CPU model)."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return (min(aff, quota) if quota else aff), aff, quota, model
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200, help="timed passes (benchmark steps) of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5))
+    ap.add_argument("--workload", type=int, default=5, choices=(1, 2, 3, 4, 5), help="headline workload")
     ap.add_argument("--driver", default="fused", choices=("fused", "per-step", "graph"),
-                    help="fused: one launch for all T steps; per-step: T launches; graph: one replay of a HIP graph "
-                         "holding the T per-step launches")
-    ap.add_argument("--cold", action="store_true", help="flush the caches before every timed launch (adds a field)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline sample")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+                    help="headline driver. fused: one launch for all T steps; per-step: T launches; graph: one replay "
+                         "of a HIP graph holding the T per-step launches")
+    ap.add_argument("--only", action="store_true", help="the headline workload alone (no per-workload table)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the threaded CPU-oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (no baseline, no bit-exact check)")
+    ap.add_argument("--profile", choices=("warm", "cold"), default=None,
+                    help="profiling run of the headline workload's launch alone: warm = K passes back to back, "
+                         "replayed from a graph of 20 (after one warm-up replay); cold = K flush-read + pass pairs")
     ap.add_argument("--plan", default=None,
-                    help="override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,REG_SLABS,"
-                         "LOADER_WAVES[,WORKGROUPS[,DU_AT_END[,BLOCK[,SLAB_ROWS[,STREAM_DU]]]]] "
+                    help="headline override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,"
+                         "REG_SLABS,LOADER_WAVES[,WORKGROUPS[,DU_AT_END[,BLOCK[,SLAB_ROWS[,STREAM_DU]]]]] "
                          "(REG_SLABS 0: slabs straight to LDS; BLOCK 16 or 32 columns per wavefront)")
     return ap.parse_args()
+
+
+class Bench:
+    """Device buffers of one workload and the timing of its passes."""
+
+    def __init__(self, g, inputs, torch, w, flush, sink):
+        from deterministic_fp32_gemm_amd.step import aligned_empty
+        self.g, self.torch, self.w = g, torch, w
+        self.flush, self.sink = flush, sink
+        self.x_h, self.dv_h, self.du_h = inputs.workload_inputs(w, "normal")
+        self.x = aligned_empty(self.x_h.size, 0)
+        self.dv = aligned_empty(self.dv_h.size, w.base_offset_bytes)
+        self.du = aligned_empty(self.du_h.size, w.base_offset_bytes)
+        self.x.copy_(torch.from_numpy(self.x_h.reshape(-1)))
+        self.dv.copy_(torch.from_numpy(self.dv_h.reshape(-1)))
+        self.reset()
+        N, C, hd, ld = w.N, w.C, w.hd, w.ld
+        self.views = (self.du.view(N, C, ld)[:, :, :hd], self.x.view(N, C, C), self.dv.view(N, C, ld)[:, :, :hd])
+        self.stream = torch.cuda.current_stream()
+
+    def reset(self):
+        self.du.copy_(self.torch.from_numpy(self.du_h.reshape(-1)))
+        self.torch.cuda.synchronize()
+
+    def step(self, plan=None):
+        du, x, dv = self.views
+        return self.g.make_step(du, x, dv, self.w.P, plan)
+
+    def pass_fn(self, step, driver, stream=None):
+        T, s = self.w.T, (self.stream if stream is None else stream)
+        if driver == "fused":
+            return lambda: step.fused(0, T, s)
+        if driver == "graph":
+            graph = step.graph(0, T, self.g.SDM_GX_STEPS_FORWARD)
+            return lambda: graph.launch(s)
+        return lambda: [step(ti, s) for ti in range(T)]
+
+    def one_pass_result(self, one_pass):
+        """d_u after one pass from the pristine inputs (host copy); d_u is reset afterwards."""
+        self.reset()
+        one_pass()
+        self.torch.cuda.synchronize()
+        out = self.du.cpu().numpy().reshape(self.du_h.shape)
+        self.reset()
+        return out
+
+    def warm_ms(self, one_pass, passes, warmup):
+        """Milliseconds per pass: `passes` passes back to back between two events on the launch stream."""
+        torch = self.torch
+        for _ in range(warmup):
+            one_pass()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(passes):
+            one_pass()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / passes
+
+    def flush_read(self):
+        self.torch.sum(self.flush, dim=0, out=self.sink)   # reads FLUSH_BYTES, writes one float
+
+    def cold_ms(self, one_pass, batch=25, pairs=7):
+        """Milliseconds per pass with cold caches: the median over `pairs` of (batch of [flush read, pass]) minus
+        (batch of [flush read]), divided by the batch size. No event sits between a flush and its pass."""
+        torch = self.torch
+
+        def timed(with_pass):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(self.stream)
+            for _ in range(batch):
+                self.flush_read()
+                if with_pass:
+                    one_pass()
+            t1.record(self.stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1)
+
+        timed(True)
+        timed(False)                                     # warm-up of both batch kinds
+        est = []
+        for _ in range(pairs):
+            a = timed(True)
+            b = timed(False)
+            est.append((a - b) / batch)
+        est.sort()
+        return est[len(est) // 2], est
+
+
+def rates(w, ms_per_pass, launches_per_pass):
+    bytes_pass, flops_pass = w.T * w.bytes_per_step, w.T * w.flops_per_step
+    s = ms_per_pass * 1e-3
+    return {"ms_per_pass": ms_per_pass, "ms_per_gx_gemm_step": ms_per_pass / w.T,
+            "ms_per_launch": ms_per_pass / launches_per_pass,
+            "gflops": flops_pass / s / 1e9, "hbm_gbps": bytes_pass / s / 1e9,
+            "frac": bytes_pass / s / 1e9 / HBM_PEAK_GBS}
+
+
+def same_bits(np, a, b):
+    return bool(((a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))).all())
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the update shards over "
-              "chunks with no exchange, so N GPUs run N independent copies of this benchmark", file=sys.stderr)
+              "chunks with no exchange, so N GPUs would run N independent copies of this benchmark", file=sys.stderr)
         return 2
     import numpy as np
     import torch
 
     import deterministic_fp32_gemm_amd as g
     from deterministic_fp32_gemm_amd import inputs
-    from deterministic_fp32_gemm_amd.step import aligned_empty
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     g.load()                                           # fails loudly if the HIP library is not built
-    dev = torch.cuda.current_device()
-    props = torch.cuda.get_device_properties(dev)
-    w = inputs.WORKLOADS[args.workload]
-    N, P, C, hd, ld, T = w.N, w.P, w.C, w.hd, w.ld, w.T
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    head = inputs.WORKLOADS[args.workload]
 
-    # ---- inputs in HBM -------------------------------------------------------------------------------------------
-    x_h, dv_h, du_h = inputs.workload_inputs(w, "normal")
-    x = aligned_empty(x_h.size, 0)
-    dv = aligned_empty(dv_h.size, w.base_offset_bytes)
-    du = aligned_empty(du_h.size, w.base_offset_bytes)
-    x.copy_(torch.from_numpy(x_h.reshape(-1)))
-    dv.copy_(torch.from_numpy(dv_h.reshape(-1)))
-    du.copy_(torch.from_numpy(du_h.reshape(-1)))
-    x3, dv3, du3 = x.view(N, C, C), dv.view(N, C, ld)[:, :, :hd], du.view(N, C, ld)[:, :, :hd]
-    plan = None
+    plan_override = None
     if args.plan:
         engine, _, fields = args.plan.partition(":")
         f = [int(v) for v in fields.split(",")]
-        plan = g.make_mfma_plan(*f) if engine == "mfma" else g.make_plan(*f)
-    step = g.make_step(du3, x3, dv3, P, plan)
-    stream = torch.cuda.current_stream()
+        plan_override = g.make_mfma_plan(*f) if engine == "mfma" else g.make_plan(*f)
 
-    graph = step.graph(0, T, g.SDM_GX_STEPS_FORWARD) if args.driver == "graph" else None
-
-    def one_pass():
-        if args.driver == "fused":
-            step.fused(0, T, stream)
-        elif args.driver == "graph":
-            graph.launch(stream)
-        else:
-            for ti in range(T):
-                step(ti, stream)
-
-    launches_per_pass = 1 if args.driver == "fused" else T
-    bytes_per_pass = T * w.bytes_per_step
-    flops_per_pass = T * w.flops_per_step
-    bytes_per_launch = bytes_per_pass / launches_per_pass
-
-    # ---- one pass of the timed configuration from the pristine d_u, kept for the CPU leg's bitwise check ----------
-    one_pass()
-    torch.cuda.synchronize()
-    gpu_one_pass = du.cpu().numpy().reshape(du_h.shape)
-    du.copy_(torch.from_numpy(du_h.reshape(-1)))
-
-    # ---- warm timing: the whole region, and every launch between its own events -------------------------------------
-    for _ in range(args.warmup):
-        one_pass()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        one_pass()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    region_ms = t0.elapsed_time(t1)
-    ms_per_step = region_ms / args.steps
-
-    # Average launch duration: the timed region over the launches it holds (back-to-back launches on one stream, so
-    # this is the kernel's own duration plus the dispatch gap, the figure a kernel trace reports as its average).
-    launch_ms_mean = region_ms / (args.steps * launches_per_pass)
-
-    # Per-launch spread: an event pair around each launch (adds the events' own overhead, ~2 us, to each figure).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(args.steps, 200) * (1 if args.driver == "graph" else launches_per_pass))]
-    k = 0
-    for _ in range(min(args.steps, 200)):
-        if args.driver in ("fused", "graph"):
-            ev[k][0].record(stream)
-            one_pass()
-            ev[k][1].record(stream)
-            k += 1
-        else:
-            for ti in range(T):
-                ev[k][0].record(stream)
-                step(ti, stream)
-                ev[k][1].record(stream)
-                k += 1
-    torch.cuda.synchronize()
-    bracketed = sorted(a.elapsed_time(b) for a, b in ev)
-    bracketed_median = bracketed[len(bracketed) // 2]
-
-    # ---- cold timing (optional): 1 GiB written between launches, outside the event pair -----------------------------
-    cold = None
-    if args.cold:
-        flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        cms = []
-        for i in range(min(args.steps, 50)):
-            flush.fill_(float(i))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            one_pass()
-            b.record(stream)
+    # ---- profiling runs: the headline launch alone ------------------------------------------------------------------
+    if args.profile:
+        b = Bench(g, inputs, torch, head, flush, sink)
+        step = b.step(plan_override)
+        one_pass = b.pass_fn(step, args.driver)
+        if args.profile == "warm":
+            # launches captured in a HIP graph (torch's stream capture of the library's kernel launches), so that the
+            # traced dispatches run back to back whatever the profiler's per-launch host cost
+            if args.driver == "graph":
+                raise SystemExit("bench.py: --profile warm takes the fused or per-step driver")
+            per_graph = 20
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn = b.pass_fn(step, args.driver, torch.cuda.current_stream())
+                for _ in range(per_graph):
+                    fn()
+            graph.replay()                               # warm-up: one replay
             torch.cuda.synchronize()
-            cms.append(a.elapsed_time(b))
-        cms.sort()
-        cmed = cms[len(cms) // 2]
-        cold = {"ms_per_step_median": cmed, "gflops": flops_per_pass / (cmed * 1e-3) / 1e9,
-                "hbm_gbps": bytes_per_pass / (cmed * 1e-3) / 1e9,
-                "frac": bytes_per_pass / (cmed * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del flush
+            reps = max(1, -(-args.steps // per_graph))
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                graph.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / (reps * per_graph)
+        else:
+            for _ in range(args.steps):
+                b.flush_read()
+                one_pass()
+            torch.cuda.synchronize()
+            ms = None
+        print(json.dumps({"profile": args.profile, "workload": head.key, "passes": args.steps,
+                          "ms_per_pass_warm": ms, "plan": step.geom["fused" if args.driver == "fused" else "step"]}),
+              flush=True)
+        return 0
 
-    # ---- CPU baseline: the oracle on whole passes of the same workload, on the host cores --------------------------
-    # The first oracle pass also checks the GPU's single pass bit for bit (NaN results by class, padding by bits).
-    cpu = None
-    bit_exact = None
+    # ---- CPU oracle (reference passes for the bit-exact checks, and the baseline) -------------------------------------
+    cpus, aff, quota, model = host_cpus()
+    oracle = None
     if not args.no_cpu:
-        import oracle
-        threads = min(16, len(os.sched_getaffinity(0)))
-        work = du_h.copy()
-        passes, t_start = 0, time.perf_counter()
-        while True:
-            used = oracle.gx_gemm_chunks(work, x_h, dv_h, 0, N, hd, threads=threads)
+        import oracle as _oracle
+        oracle = _oracle
+
+    def oracle_pass(b, threads):
+        want = b.du_h.copy()
+        t = time.perf_counter()
+        oracle.gx_gemm_chunks(want, b.x_h, b.dv_h, 0, b.w.N, b.w.hd, threads=threads)
+        return want, time.perf_counter() - t
+
+    # ---- per-workload table (headline included) ------------------------------------------------------------------------
+    keys = [head.key] if args.only else sorted({2, 3, 4, 5, head.key})
+    table = {}
+    headline = None
+    for key in keys:
+        w = inputs.WORKLOADS[key]
+        b = Bench(g, inputs, torch, w, flush, sink)
+        want = oracle_pass(b, cpus)[0] if oracle else None
+        row = {"description": w.description}
+        passes = max(20, args.steps if key == head.key else min(args.steps, 200))
+        for name in ("default", "valu"):
+            if name == "valu" and key == head.key and plan_override is not None:
+                continue
+            if name == "default":
+                step = b.step(plan_override if key == head.key else None)
+            else:                                          # the vector-ALU engine's plan for the fused launch
+                step = b.step(g.sdm_gx_plan(w.N, w.C, w.hd, w.ld, w.ld, 0, w.base_offset_bytes % 16,
+                                            g.SDM_GX_ENGINE_VALU))
+            fused = b.pass_fn(step, "fused")
+            e = {"plan": step.geom["fused"], "kernel": kernel_name(step.geom["fused"])}
+            got = b.one_pass_result(fused)
+            e["bit_exact"] = same_bits(np, got, want) if want is not None else None
+            e["warm"] = rates(w, b.warm_ms(fused, passes, args.warmup), 1)
+            b.reset()
+            if name == "default":
+                cms, est = b.cold_ms(fused)
+                e["cold"] = rates(w, cms, 1)
+                e["cold"]["per_pair_ms"] = est
+                b.reset()
+                per = b.pass_fn(step, "per-step")
+                got = b.one_pass_result(per)
+                e["per_step_driver"] = rates(w, b.warm_ms(per, max(20, passes // 4), 5), w.T)
+                e["per_step_driver"]["plan"] = step.geom["step"]
+                e["per_step_driver"]["bit_exact"] = same_bits(np, got, want) if want is not None else None
+                b.reset()
+                if key == head.key:
+                    one_pass = b.pass_fn(step, args.driver)
+                    if args.driver != "fused":
+                        got = b.one_pass_result(one_pass)
+                        hb = same_bits(np, got, want) if want is not None else None
+                    else:
+                        hb = e["bit_exact"]
+                    launches = 1 if args.driver == "fused" else w.T
+                    ms = b.warm_ms(one_pass, args.steps, args.warmup) if args.driver != "fused" else \
+                        e["warm"]["ms_per_pass"]
+                    headline = dict(b=b, step=step, ms=ms, launches=launches, bit_exact=hb, cold=e["cold"],
+                                    per_step=e["per_step_driver"],
+                                    plan=step.geom["fused" if args.driver == "fused" else "step"])
+            row[name] = e
+            print(f"bench: workload {key} {name}: {e['kernel']} warm {e['warm']['ms_per_pass'] * 1e3:.2f} us/pass "
+                  f"(frac {e['warm']['frac']:.3f})" + (f", cold {e['cold']['ms_per_pass'] * 1e3:.2f} us/pass "
+                                                      f"(frac {e['cold']['frac']:.3f})" if "cold" in e else "")
+                  + f", bit_exact {e['bit_exact']}", file=sys.stderr, flush=True)
+        # yardstick: a device copy moving the pass's algorithmic bytes (half read, half written), same cold protocol
+        src = torch.empty(w.T * w.bytes_per_step // 8, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        copy = lambda: dst.copy_(src)                  # noqa: E731
+        row["copy_yardstick"] = {"bytes": w.T * w.bytes_per_step,
+                                 "warm": rates(w, b.warm_ms(copy, passes, args.warmup), 1),
+                                 "cold": rates(w, b.cold_ms(copy)[0], 1)}
+        del src, dst
+        table[str(key)] = row
+        if key != head.key:
+            del b
+
+    # ---- CPU baseline: the oracle on whole passes of the headline workload ---------------------------------------------
+    cpu = None
+    if oracle:
+        b = headline["b"]
+        passes, el = 0, 0.0
+        while el < args.cpu_seconds:
+            el += oracle_pass(b, cpus)[1]
             passes += 1
-            if passes == 1:
-                t_check = time.perf_counter()
-                same = (gpu_one_pass.view(np.uint32) == work.view(np.uint32)) | (
-                    np.isnan(gpu_one_pass) & np.isnan(work))
-                bit_exact = bool(same.all())
-                t_start += time.perf_counter() - t_check
-            if time.perf_counter() - t_start >= args.cpu_seconds:
-                break
-        el = time.perf_counter() - t_start
-        cpu = {"value": round(passes * flops_per_pass / el / 1e9, 3), "unit": "GFLOP/s", "cores": used,
-               "kind": "oracle",
-               "sample": f"{passes} full passes of the workload ({T} steps x {P} chunks) in {el:.1f} s, chunks "
-                         f"split over {used} host threads, scalar fmaf chain",
-               "hbm_gbps_equiv": round(passes * bytes_per_pass / el / 1e9, 3)}
+        flops_pass, bytes_pass = head.T * head.flops_per_step, head.T * head.bytes_per_step
+        # one thread, the scalar oracle as it stands, over as many whole chunks as fit about a fifth of the budget
+        n1, el1 = 0, 0.0
+        sub = b.du_h.copy()
+        while el1 < args.cpu_seconds / 5 and n1 < head.N:
+            k = min(head.P, head.N - n1)
+            t = time.perf_counter()
+            oracle.gx_gemm_chunks(sub, b.x_h, b.dv_h, n1, n1 + k, head.hd, threads=1)
+            el1 += time.perf_counter() - t
+            n1 += k
+        flops_chunk = flops_pass / head.N
+        cpu = {"value": round(passes * flops_pass / el / 1e9, 3), "unit": "GFLOP/s", "cores": cpus, "kind": "oracle",
+               "sample": f"{passes} full passes of workload {head.key} ({head.T} steps x {head.P} chunks) in "
+                         f"{el:.1f} s, chunks split over {cpus} host threads (one per CPU this process may use), "
+                         f"the unchanged scalar fmaf chain",
+               "hbm_gbps_equiv": round(passes * bytes_pass / el / 1e9, 3),
+               "single_thread": {"value": round(n1 * flops_chunk / el1 / 1e9, 3), "unit": "GFLOP/s",
+                                 "sample": f"{n1} chunks of workload {head.key} in {el1:.1f} s on one thread"},
+               "host": {"cpu_model": model, "affinity_cpus": aff, "cgroup_cpu_quota": quota}}
 
-    # ---- roofline of the dominant kernel ------------------------------------------------------------------------------
-    t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
-    t_alu = (flops_per_pass / launches_per_pass) / (VALU_FP32_PEAK_TFLOPS * 1e12)
-    launch_s = launch_ms_mean * 1e-3
+    # ---- headline line ----------------------------------------------------------------------------------------------------
+    w = head
+    launches = headline["launches"]
+    ms_pass = headline["ms"]
+    bytes_launch = w.T * w.bytes_per_step / launches
+    flops_launch = w.T * w.flops_per_step / launches
+    launch_s = ms_pass / launches * 1e-3
+    t_hbm = bytes_launch / (HBM_PEAK_GBS * 1e9)
+    t_alu = flops_launch / (VALU_FP32_PEAK_TFLOPS * 1e12)
+    plan = headline["plan"]
     if t_hbm >= t_alu:
-        roof = {"bound": "hbm", "achieved": bytes_per_launch / launch_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": bytes_launch / launch_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "alu", "achieved": flops_per_pass / launches_per_pass / launch_s / 1e12,
-                "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof = {"bound": "alu", "achieved": flops_launch / launch_s / 1e12, "peak": VALU_FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.key, args.driver, step.geom["fused" if args.driver == "fused" else "step"])
-    roof["kernel"] = kernel_name(step.geom["fused" if args.driver == "fused" else "step"])
-    roof["algorithmic_bytes_per_launch"] = bytes_per_launch
-    roof["algorithmic_flops_per_launch"] = flops_per_pass / launches_per_pass
-    roof["launch_ms_mean"] = launch_ms_mean
-    roof["bracketed_launch_ms_median"] = bracketed_median
-    roof["bracketed_launch_ms_min"] = bracketed[0]
-
-    gflops = flops_per_pass / (ms_per_step * 1e-3) / 1e9
+    roof["traffic"] = measured_traffic(w.key, args.driver, plan)
+    roof["kernel"] = kernel_name(plan)
+    roof["algorithmic_bytes_per_launch"] = bytes_launch
+    roof["algorithmic_flops_per_launch"] = flops_launch
+    roof["launch_ms_mean"] = ms_pass / launches
+    roof["cold_frac"] = headline["cold"]["frac"] if launches == 1 else None
+    gflops = w.T * w.flops_per_step / (ms_pass * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(gflops, 3),
@@ -257,20 +430,24 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": ms_pass,
+        "ms_per_gx_gemm_step": ms_pass / w.T,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"workload {w.key}: {w.description}", "T": T, "P": P, "N": N, "C": C, "hd": hd,
-                   "ld": ld, "base_offset_bytes": w.base_offset_bytes, "driver": args.driver, "pattern": "normal",
-                   "plan": step.geom["fused" if args.driver == "fused" else "step"]},
-        "hbm_gbps": round(bytes_per_pass / (ms_per_step * 1e-3) / 1e9, 3),
-        "bit_exact": bit_exact,
+        "config": {"workload": f"workload {w.key}: {w.description}", "T": w.T, "P": w.P, "N": w.N, "C": w.C,
+                   "hd": w.hd, "ld": w.ld, "base_offset_bytes": w.base_offset_bytes, "driver": args.driver,
+                   "pattern": "normal", "bench_step": f"one pass over the workload: its {w.T} gx_gemm steps",
+                   "plan": plan},
+        "hbm_gbps": round(w.T * w.bytes_per_step / (ms_pass * 1e-3) / 1e9, 3),
+        "bit_exact": headline["bit_exact"],
         "roofline": roof,
+        "cold": headline["cold"],
+        "per_step_driver": headline["per_step"],
+        "workloads": table,
         "cpu_baseline": cpu,
-        "cold": cold,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
     }
     print(json.dumps(out), flush=True)

@@ -120,3 +120,9 @@ def step(d_u, x, d_dv, ti: int, P: int, hd: int):
                     acc = fma(x[n][j][i], d_dv[n][j][c], acc)
                 out[n][i][c] = add(d_u[n][i][c], acc)
     return out
+
+
+def mul(a: float, b: float) -> float:
+    """binary32 multiplication with one rounding: a*b + (-0) is a*b exactly for every a, b (a +0 product stays +0, a
+    -0 product stays -0), so one fused rounding of it is the rounded product."""
+    return fma(a, b, -0.0)

@@ -2,8 +2,9 @@
 
 The operation (page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_gemm_cuda.py", module docstring): for
 every chunk n = ti*P + p of step ti, row i < C and column c < hd, d_u[n, i, c] += acc with
-acc = fmaf(x[n, j, i], d_dv[n, j, c], acc) over j = 0..C-1 from +0 and one separately rounded add. The C ABI is in
-include/sdm_gx_gemm.h; the functions below carry the same names and only marshal arguments.
+acc = fmaf(x[n, j, i], d_dv[n, j, c], acc) over j = 0..C-1 from +0 and one separately rounded add. Phase A, the
+consumer of the updated d_u (page "... gx_pa2_cuda.py", gx_pa2_kernel), is in the same library. The C ABI is in
+include/sdm_gx_gemm.h and include/sdm_gx_pa2.h; the functions below carry the same names and only marshal arguments.
 """
 
 from ._binding import (  # noqa: F401
@@ -49,5 +50,13 @@ from ._binding import (  # noqa: F401
     sdm_gx_plan_t,
     sdm_gx_prepare,
     sdm_gx_strerror,
+    make_pa2_plan,
+    pa2_args,
+    sdm_pa2_args_t,
+    sdm_pa2_check,
+    sdm_pa2_plan_for,
+    sdm_pa2_plan_t,
+    sdm_pa2_step,
+    sdm_pa2_steps,
 )
 from .step import make_step, tensor_layout  # noqa: F401

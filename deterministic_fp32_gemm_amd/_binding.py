@@ -65,16 +65,38 @@ class sdm_gx_launch_t(ctypes.Structure):
                 ("plan_step", sdm_gx_plan_t), ("plan_fused", sdm_gx_plan_t)]
 
 
+class sdm_pa2_args_t(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("bank", ctypes.c_void_p), ("slots", ctypes.c_int64),
+                ("snap", ctypes.c_void_p), ("snap_rows", ctypes.c_int64), ("ssr", ctypes.c_int64),
+                ("d_u", ctypes.c_void_p), ("ld_u", ctypes.c_int64), ("beta", ctypes.c_void_p),
+                ("kpay", ctypes.c_void_p), ("rec", ctypes.c_void_p), ("bpre", ctypes.c_void_p),
+                ("out_eff", ctypes.c_void_p), ("out_g", ctypes.c_void_p), ("plane", ctypes.c_int64),
+                ("planes", ctypes.c_int64), ("N", ctypes.c_int64), ("P", ctypes.c_int64), ("C", ctypes.c_int64),
+                ("W", ctypes.c_int64), ("hd", ctypes.c_int64)]
+
+
+class sdm_pa2_plan_t(ctypes.Structure):
+    _fields_ = [("slices_per_wave", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("tile_len", ctypes.c_int32),
+                ("ctas", ctypes.c_int32), ("npair", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 EXPORTS = ("sdm_gx_gemm", "sdm_gx_gemm_ex", "sdm_gx_gemm_steps", "sdm_gx_check", "sdm_gx_plan", "sdm_gx_plan_for",
            "sdm_gx_plan_complete", "sdm_gx_prepare", "sdm_gx_launch", "sdm_gx_launch_fused", "sdm_gx_graph_create",
            "sdm_gx_graph_launch", "sdm_gx_graph_nodes", "sdm_gx_graph_destroy", "sdm_gx_kernel_attrs",
-           "sdm_gx_strerror", "sdm_gx_last_hip_error", "sdm_gx_abi_version")
+           "sdm_gx_strerror", "sdm_gx_last_hip_error", "sdm_gx_abi_version",
+           "sdm_pa2_check", "sdm_pa2_plan_for", "sdm_pa2_step", "sdm_pa2_steps")
 
 _lib = None
 _lock = threading.Lock()
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _PP = ctypes.POINTER(sdm_gx_plan_t)
 _LP = ctypes.POINTER(sdm_gx_launch_t)
+_AP = ctypes.POINTER(sdm_pa2_args_t)
+_QP = ctypes.POINTER(sdm_pa2_plan_t)
 
 
 def lib_path() -> str:
@@ -112,6 +134,10 @@ def load() -> ctypes.CDLL:
             "sdm_gx_graph_launch": [_vp, _vp],
             "sdm_gx_graph_nodes": [_vp],
             "sdm_gx_graph_destroy": [_vp],
+            "sdm_pa2_check": [_AP, _i64],
+            "sdm_pa2_plan_for": [_AP, _i32, _i32, _QP],
+            "sdm_pa2_step": [_AP, _i64, _QP, _vp],
+            "sdm_pa2_steps": [_AP, _i64, _i64, _i32, _QP, _vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -320,3 +346,61 @@ def sdm_gx_last_hip_error() -> int:
 
 def sdm_gx_abi_version() -> int:
     return load().sdm_gx_abi_version()
+
+
+# ---- Phase A (sdm_gx_pa2.h) ---------------------------------------------------------------------------------------------
+def _iptr(t, name: str) -> int:
+    """Device address of an int32 tensor (or a plain integer)."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda:
+        raise TypeError(f"{name}: an int32 GPU tensor or a device address")
+    return t.data_ptr()
+
+
+def pa2_args(grad, bank, snap, ssr, d_u, beta, kpay, rec, bpre, out_eff, out_g, P, C, W, hd=None,
+             ld_u=None) -> sdm_pa2_args_t:
+    """An sdm_pa2_args_t from torch tensors: grad, bank [slots, hd]; snap [rows, hd]; d_u [N*C, ld_u] (a [N, C, hd]
+    view with row stride ld_u also works); beta [N*C]; kpay [N, n], rec [N, n, 4], bpre [N, nb+1] int32 (bpre None
+    for per-entry rows); out_eff, out_g [planes, plane]. Sizes are read from the tensors' shapes and strides."""
+    a = sdm_pa2_args_t()
+    hd = int(grad.shape[-1]) if hd is None else int(hd)
+    a.grad, a.bank, a.snap = _ptr(grad, "grad"), _ptr(bank, "bank"), _ptr(snap, "snap")
+    a.slots, a.snap_rows, a.ssr = int(grad.shape[0]), int(snap.numel() // max(1, int(snap.shape[-1]))), int(ssr)
+    a.d_u, a.beta = _ptr(d_u, "d_u"), _ptr(beta, "beta")
+    a.ld_u = int(ld_u if ld_u is not None else d_u.stride(-2))
+    a.kpay, a.rec, a.bpre = _iptr(kpay, "kpay"), _iptr(rec, "rec"), _iptr(bpre, "bpre")
+    a.out_eff, a.out_g = _ptr(out_eff, "out_eff"), _ptr(out_g, "out_g")
+    a.planes, a.plane = int(out_eff.shape[0]), int(out_eff.shape[1])
+    a.N, a.P, a.C, a.W, a.hd = int(kpay.shape[0]), int(P), int(C), int(W), hd
+    return a
+
+
+def make_pa2_plan(slices_per_wave, waves_per_wg, tile_len) -> sdm_pa2_plan_t:
+    p = sdm_pa2_plan_t()
+    p.slices_per_wave, p.waves_per_wg, p.tile_len = slices_per_wave, waves_per_wg, tile_len
+    return p
+
+
+def sdm_pa2_check(args: sdm_pa2_args_t, ti) -> int:
+    """The status code (no exception); no device access."""
+    return load().sdm_pa2_check(ctypes.byref(args), int(ti))
+
+
+def sdm_pa2_plan_for(args: sdm_pa2_args_t, num_cus=256, lds_limit=160 * 1024) -> sdm_pa2_plan_t:
+    p = sdm_pa2_plan_t()
+    _raise(load().sdm_pa2_plan_for(ctypes.byref(args), int(num_cus), int(lds_limit), ctypes.byref(p)), "sdm_pa2_plan_for")
+    return p
+
+
+def sdm_pa2_step(args: sdm_pa2_args_t, ti, plan=None, stream=None) -> None:
+    _raise(load().sdm_pa2_step(ctypes.byref(args), int(ti), ctypes.byref(plan) if plan is not None else None,
+                               _stream(stream)), "sdm_pa2_step")
+
+
+def sdm_pa2_steps(args: sdm_pa2_args_t, ti_begin, ti_end, mode=SDM_GX_STEPS_FORWARD, plan=None, stream=None) -> None:
+    _raise(load().sdm_pa2_steps(ctypes.byref(args), int(ti_begin), int(ti_end), int(mode),
+                                ctypes.byref(plan) if plan is not None else None, _stream(stream)), "sdm_pa2_steps")

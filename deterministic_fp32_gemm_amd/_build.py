@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libsdm_gx_gemm.so")
-SOURCES = ("gx_gemm_kernel.hip", "gx_gemm_mfma.hip", "gx_gemm_api.cpp")
+SOURCES = ("gx_gemm_kernel.hip", "gx_gemm_mfma.hip", "gx_gemm_api.cpp", "gx_pa2_kernel.hip", "gx_pa2_api.cpp")
 
 # Numerics-relevant flags: no contraction or fast-math (the chain's fmaf and the final add are what runs), f32
 # denormals kept, and no packed-FP32 instructions (scalar v_fma_f32 / v_fmac_f32 only).

@@ -28,6 +28,15 @@ int hip_fail(hipError_t e) {
 
 constexpr uint64_t kLaunchMagic = 0x314843554E4C4753ull;   // prepared-launch tag
 
+}  // namespace
+
+namespace sdm_gx {
+// The HIP error behind an SDM_GX_ERR_HIP status of any entry point of the library (Phase A's included).
+int record_hip_error(hipError_t e) { return hip_fail(e); }
+}  // namespace sdm_gx
+
+namespace {
+
 // ---- argument checks (no device access) ---------------------------------------------------------------------------
 int64_t row_extent(int64_t N, int64_t C, int64_t ld, int64_t hd) {   // elements reachable in a [N][C] ld-strided array
     return (N * C - 1) * ld + hd;

@@ -1,0 +1,265 @@
+// Phase A of the deterministic backward step on gfx950: the consumer of the updated d_u.
+//
+// Operation (page "sparse-delta-memory 2.0.0 -- sparse_delta_memory/cuda/gx_pa2_cuda.py", gx_pa2_kernel, float32
+// grad / bank / snapshot rows): for chunk k = ti*P + p and each 128-column slice of the head, the chunk's n = C*W
+// records are walked in order. A group opens at a FIRST record (acc = +0; at a valid FIRST the group's grad row gdw
+// and snapshot row sn are read, else both are +0); every record adds sck * x to acc with one fmaf per column (x: the
+// record's token row of d_u); each record's dot(x, sn) and the group's dot(gdw, sn) are a fmul + 3 fmaf chain over a
+// lane's 4 columns followed by the balanced pairwise sum over the slice's 32 lanes (padding lanes and columns +0); a
+// valid LAST record stores grad = fmaf(gdw, cpe, acc) and bank = sn; each record writes -beta[t] * dot and cpe * g
+// (the raw dot and g into per-slice planes when the head has several slices; +0 for INVALID records).
+//
+// gfx950 structure:
+//   * A wavefront holds two of the page's 32-lane warps: lanes 0-31 are slice 2q's lanes, lanes 32-63 slice 2q+1's
+//     (SG = 2), each lane 4 columns, so one record's walk covers 256 columns; with SG = 1 (one slice, or C > 128 where
+//     two slices of token rows would not fit in LDS) lanes 32-63 hold no columns.
+//   * A workgroup of WAVES wavefronts takes one (chunk, slice pair) and a range of tiles: it stages the chunk's token
+//     rows of d_u (C rows of the pair's columns) and its beta values in LDS once; wavefront w walks tile
+//     cta*WAVES + w: records [snap_back(tile*L), snap_back((tile+1)*L)), tile boundaries moved back to a group's
+//     FIRST through the payload's distance field (the page's snap_back), so every group is walked by one wavefront.
+//   * Records are loaded 64 at a time (lane l: record jb + l) and broadcast with readlane; the 32-lane sums are four
+//     DPP adds (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror) and a ds_swizzle swap of the
+//     16-lane halves. After each xor-butterfly level every lane of an aligned block holds the same block sum, so
+//     pairing a lane with any lane of the partner block (the mirrors) gives the page's tree, bit for bit.
+//   * Per record, lane k of the batch collects the record's values (compare and select), so each batch writes its
+//     outputs with one store per plane.
+//   * Record fields are bounds-checked before any access they steer (token < C, write < W, slot < slots, snapshot
+//     row < snap_rows): a record outside the definition gives unspecified values but never reaches outside the
+//     buffers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gx_pa2.h"
+
+namespace sdm_gx {
+namespace {
+
+constexpr uint32_t kFirst = 0x80000000u;
+constexpr uint32_t kLast = 0x40000000u;
+constexpr uint32_t kInvalid = 0x00020000u;
+constexpr int kDistShift = 18;
+constexpr uint32_t kDistMax = 4095u;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// the balanced pairwise sum over each 32-lane half, in lane order; every lane of the half gets it
+__device__ __forceinline__ float tree32(float v) {
+    v = v + dpp<0xB1>(v);          // quad_perm [1,0,3,2]: lanes l, l^1
+    v = v + dpp<0x4E>(v);          // quad_perm [2,3,0,1]: 2-blocks
+    v = v + dpp<0x141>(v);         // row_half_mirror: 4-blocks of an 8-lane half row
+    v = v + dpp<0x140>(v);         // row_mirror: 8-blocks of a 16-lane row
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));   // 16-blocks
+    return v;
+}
+
+// fmul then three fmaf over a lane's 4 columns
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+    float s = a.x * b.x;
+    s = __builtin_fmaf(a.y, b.y, s);
+    s = __builtin_fmaf(a.z, b.z, s);
+    s = __builtin_fmaf(a.w, b.w, s);
+    return s;
+}
+
+// nv (0..4) floats of a row from column position p (4-byte aligned), +0 past them
+__device__ __forceinline__ f32x4 load_cols(const float* p, int nv) {
+    if (nv == 4) {
+        const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
+        return f32x4{v.x, v.y, v.z, v.w};
+    }
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (nv > 0) v.x = p[0];
+    if (nv > 1) v.y = p[1];
+    if (nv > 2) v.z = p[2];
+    return v;
+}
+
+__device__ __forceinline__ void store_cols(float* p, f32x4 v, int nv) {
+    if (nv == 4) {
+        *reinterpret_cast<f32x4u*>(p) = f32x4u{v.x, v.y, v.z, v.w};
+        return;
+    }
+    if (nv > 0) p[0] = v.x;
+    if (nv > 1) p[1] = v.y;
+    if (nv > 2) p[2] = v.z;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The FIRST position of the group holding position j (0 for j <= 0, n for j >= n): the payload's distance field, or
+// for distances of kDistMax and more a scan back 64 records at a time. Wavefront-uniform.
+__device__ __forceinline__ int snap_back(const int32_t* kp, int j, int n, int lane) {
+    if (j <= 0) return 0;
+    if (j >= n) return n;
+    const uint32_t p = static_cast<uint32_t>(uniform(kp[j]));
+    if (p & kFirst) return j;
+    const uint32_t d = (p >> kDistShift) & kDistMax;
+    if (d < kDistMax) return j - static_cast<int>(d);
+    for (int base = j - static_cast<int>(kDistMax);; base -= 64) {      // ends: q <= 0 holds for every lane at last
+        const int q = base - lane;
+        const bool f = q <= 0 || (static_cast<uint32_t>(kp[q > 0 ? q : 0]) & kFirst);
+        const uint64_t m = __ballot(f);
+        if (m) {
+            const int r = base - static_cast<int>(__builtin_ctzll(m));
+            return r > 0 ? r : 0;
+        }
+    }
+}
+
+template <int SG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
+    extern __shared__ f32x4 tok_s[];                   // [C][32 * SG] token rows, then beta [C]
+    float* const beta_s = reinterpret_cast<float*>(tok_s + a.C * 32 * SG);
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
+    const int half = lane >> 5, hl = lane & 31;
+    int b = static_cast<int>(blockIdx.x);
+    const int cta = b % a.ctas;
+    b /= a.ctas;
+    const int sp = b % a.npair;
+    const int p = b / a.npair;
+    const int C = a.C, W = a.W, n = a.n, hd = a.hd;
+    const int64_t chunk = static_cast<int64_t>(a.ti) * a.P + p;
+    const int sl = sp * SG + (SG == 2 ? half : 0);     // this lane's slice
+    const bool lane_slice = SG == 2 ? sl < a.nsl : half == 0;
+    const int col0 = sl * a.slw + 4 * hl;
+    const bool on = lane_slice && 4 * hl < a.slw && col0 < hd;
+    const int nv = on ? (hd - col0 < 4 ? hd - col0 : 4) : 0;
+    const int tl = SG == 2 ? lane : hl;                // this lane's entry of a token row in LDS
+
+    // stage the chunk's token rows (the pair's columns, +0 past the slice or the head) and beta
+    const float* rows = a.du + chunk * C * a.ld_u;
+    for (int t = wave; t < C; t += WAVES) {
+        const f32x4 v = on ? load_cols(rows + static_cast<int64_t>(t) * a.ld_u + col0, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (SG == 2 || half == 0) tok_s[t * 32 * SG + tl] = v;
+    }
+    for (int i = static_cast<int>(threadIdx.x); i < C; i += 64 * WAVES) beta_s[i] = a.beta[chunk * C + i];
+    __syncthreads();
+
+    const int32_t* kp = a.kpay + chunk * n;
+    const int32_t* rp = a.rec + chunk * n * 4;
+    const int tile = cta * WAVES + wave;
+    const int64_t t0 = static_cast<int64_t>(tile) * a.L;
+    const int s = snap_back(kp, t0 < n ? static_cast<int>(t0) : n, n, lane);
+    const int e = snap_back(kp, t0 + a.L < n ? static_cast<int>(t0 + a.L) : n, n, lane);
+    if (s >= e) return;                                // no barrier follows
+
+    // dense snapshot rows: the ordinal of the tile's first valid FIRST (block prefix + valid FIRSTs in the block
+    // before s)
+    int gw = 0;
+    if (a.ssr < 0) {
+        const int bs = s >> 5;
+        const int q = 32 * bs + lane;
+        const uint32_t pq = (lane < 32 && q < s) ? static_cast<uint32_t>(kp[q]) : 0u;
+        gw = a.bpre[chunk * ((n + 31) / 32 + 1) + bs] +
+             static_cast<int>(__builtin_popcountll(__ballot((pq & kFirst) && !(pq & kInvalid))));
+        gw = uniform(gw);
+    }
+    const int64_t srow_base = a.ssr < 0 ? chunk * n : static_cast<int64_t>(a.ti) * a.ssr + static_cast<int64_t>(p) * n;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gdw = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
+    float g = 0.f;                                     // the group's dot(gdw, sn), per half
+    const int64_t obase = chunk * n;
+    for (int jb = s; jb < e; jb += 64) {
+        const int nrec = e - jb < 64 ? e - jb : 64;
+        int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+        if (lane < nrec) {                             // 16-byte records, 16-byte aligned (checked on the host)
+            const int4 q = reinterpret_cast<const int4*>(rp)[jb + lane];
+            r0 = q.x;
+            r1 = q.y;
+            r2 = q.z;
+            r3 = q.w;
+        }
+        float effA = 0.f, effB = 0.f, gA = 0.f, gB = 0.f;
+        for (int k = 0; k < nrec; ++k) {
+            const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
+            int tok = static_cast<int>((pay >> 9) & 0xFFu);
+            tok = tok < C ? tok : C - 1;
+            const float sck = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r2, k));
+            f32x4 x = tok_s[tok * 32 * SG + tl];
+            if (!on) x = f32x4{0.f, 0.f, 0.f, 0.f};
+            const bool valid = !(pay & kInvalid);
+            if (pay & kFirst) {
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                gdw = f32x4{0.f, 0.f, 0.f, 0.f};
+                sn = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (valid) {
+                    const int64_t slot = __builtin_amdgcn_readlane(r1, k);
+                    const int64_t srow = a.ssr < 0 ? srow_base + gw
+                                                   : srow_base + static_cast<int64_t>(tok) * W + (pay & 0xFFu);
+                    ++gw;
+                    if (on && slot >= 0 && slot < a.slots) gdw = load_cols(a.grad + slot * hd + col0, nv);
+                    if (on && srow < a.snap_rows) sn = load_cols(a.snap + srow * hd + col0, nv);
+                }
+                g = tree32(dot4(gdw, sn));
+            }
+            acc.x = __builtin_fmaf(sck, x.x, acc.x);
+            acc.y = __builtin_fmaf(sck, x.y, acc.y);
+            acc.z = __builtin_fmaf(sck, x.z, acc.z);
+            acc.w = __builtin_fmaf(sck, x.w, acc.w);
+            const float dot = tree32(dot4(x, sn));
+            if ((pay & kLast) && valid) {
+                const int64_t slot = __builtin_amdgcn_readlane(r1, k);
+                const float cpe = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r3, k));
+                if (on && slot >= 0 && slot < a.slots) {
+                    f32x4 o;
+                    o.x = __builtin_fmaf(gdw.x, cpe, acc.x);
+                    o.y = __builtin_fmaf(gdw.y, cpe, acc.y);
+                    o.z = __builtin_fmaf(gdw.z, cpe, acc.z);
+                    o.w = __builtin_fmaf(gdw.w, cpe, acc.w);
+                    store_cols(a.grad + slot * hd + col0, o, nv);
+                    store_cols(a.bank + slot * hd + col0, sn, nv);
+                }
+            }
+            const float dA = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dot), 0));
+            const float dB = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dot), 32));
+            const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 0));
+            const float g1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 32));
+            if (lane == k) {
+                effA = dA;
+                effB = dB;
+                gA = g0;
+                gB = g1;
+            }
+        }
+        // outputs of records jb .. jb + nrec - 1 (lane l: record jb + l)
+        if (lane < nrec) {
+            const uint32_t pay = static_cast<uint32_t>(r0);
+            const int tok = static_cast<int>((pay >> 9) & 0xFFu), w = static_cast<int>(pay & 0xFFu);
+            if (tok < C && w < W) {
+                const bool valid = !(pay & kInvalid);
+                const int64_t o = obase + static_cast<int64_t>(tok) * W + w;
+                if (a.nsl == 1) {
+                    a.out_eff[o] = valid ? (-beta_s[tok]) * effA : 0.f;
+                    a.out_g[o] = valid ? __builtin_bit_cast(float, r3) * gA : 0.f;
+                } else {
+                    const int s0 = sp * SG;
+                    a.out_eff[s0 * a.plane + o] = valid ? effA : 0.f;
+                    a.out_g[s0 * a.plane + o] = valid ? gA : 0.f;
+                    if (SG == 2 && s0 + 1 < a.nsl) {
+                        a.out_eff[(s0 + 1) * a.plane + o] = valid ? effB : 0.f;
+                        a.out_g[(s0 + 1) * a.plane + o] = valid ? gB : 0.f;
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+const void* find_pa2_kernel(int slices_per_wave, int waves) {
+#define SDM_PA2_K(SG, WV) \
+    if (slices_per_wave == SG && waves == WV) return reinterpret_cast<const void*>(&gx_pa2_kernel<SG, WV>);
+    SDM_PA2_K(1, 4) SDM_PA2_K(1, 8) SDM_PA2_K(1, 16) SDM_PA2_K(2, 4) SDM_PA2_K(2, 8) SDM_PA2_K(2, 16)
+#undef SDM_PA2_K
+    return nullptr;
+}
+
+}  // namespace sdm_gx

@@ -14,11 +14,12 @@ from deterministic_fp32_gemm_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sdm_gx_gemm.h")
+HEADERS = (HEADER, os.path.join(ROOT, "include", "sdm_gx_pa2.h"))
 
 
 def header_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"SDM_GX_API\s+(?:const\s+)?\w+\*?\s+\*?(sdm_gx_\w+)\s*\(", text)))
+    text = "".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"SDM_GX_API\s+(?:const\s+)?\w+\*?\s+\*?(sdm_(?:gx|pa2)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():

@@ -57,6 +57,7 @@ def test_every_kernel_instance_has_no_scratch_and_no_spills(tmp_path):
     assert sum("gx_chain_kernel" in n for n in names) == 134
     assert sum("gx_mfma_kernel" in n for n in names) == 28
     assert sum("gx_mfma_dma_kernel" in n for n in names) == 59
+    assert sum("gx_pa2_kernel" in n for n in names) == 6
     for name, f in found:
         assert f.get(".private_segment_fixed_size") == "0", name
         assert f.get(".vgpr_spill_count") == "0" and f.get(".sgpr_spill_count") == "0", name

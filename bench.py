@@ -15,6 +15,8 @@ What the line holds:
   workloads                        workloads 2-5: both engines warm, the default engine cold and per step, each
                                    pass checked bit for bit against the CPU oracle; and a device copy of the same
                                    bytes (half read, half written) warm and cold, as a streaming yardstick
+  phase_a                          Phase A, the consumer of the updated d_u, on synthetic records shaped like workloads
+                                   3 and 5 (T steps, one launch each), warm and cold, checked against its oracle
   cpu_baseline                     the CPU oracle, unchanged, on this host's cores (and on one core)
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--driver fused|per-step|graph]
@@ -118,9 +120,13 @@ def parse():
     ap.add_argument("--only", action="store_true", help="the headline workload alone (no per-workload table)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the threaded CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (no baseline, no bit-exact check)")
-    ap.add_argument("--profile", choices=("warm", "cold"), default=None,
-                    help="profiling run of the headline workload's launch alone: warm = K passes back to back, "
-                         "replayed from a graph of 20 (after one warm-up replay); cold = K flush-read + pass pairs")
+    ap.add_argument("--no-phase-a", action="store_true", help="skip the Phase A leg")
+    ap.add_argument("--phase-a", default=None, choices=("a3", "a5"),
+                    help="with --profile: profile this Phase A workload's pass instead of the update")
+    ap.add_argument("--profile", choices=("warm", "graph", "cold"), default=None,
+                    help="profiling run of the headline workload's launch alone: warm = W + K passes launched back to "
+                         "back from the host, as the benchmark times them; graph = K passes replayed from a graph of "
+                         "20 (after one warm-up replay); cold = K flush-read + pass pairs")
     ap.add_argument("--plan", default=None,
                     help="headline override: valu:RI,RC,WAVES,STAGING,XCD[,SLAB] or mfma:ROW_WAVES,COL_WAVES,STAGES,"
                          "REG_SLABS,LOADER_WAVES[,WORKGROUPS[,DU_AT_END[,BLOCK[,SLAB_ROWS[,STREAM_DU]]]]] "
@@ -216,6 +222,64 @@ class Bench:
         return est[len(est) // 2], est
 
 
+class Pa2Bench:
+    """Phase A (the consumer of the updated d_u) on one synthetic record workload: device buffers, one pass = the T
+    steps in order, one launch each (steps are sequential: a step reads grad rows earlier steps wrote)."""
+
+    def __init__(self, g, torch, key):
+        import numpy as np
+
+        from deterministic_fp32_gemm_amd import pa2_inputs as PI
+        from deterministic_fp32_gemm_amd.step import aligned_empty
+        self.g, self.torch = g, torch
+        self.w = w = PI.PA2_WORKLOADS[key]
+        self.h = h = PI.inputs(w, "normal")
+        self.grad = torch.from_numpy(h["grad"]).cuda()
+        self.bank = torch.from_numpy(h["bank"]).cuda()
+        self.snap = torch.from_numpy(h["snap"]).cuda()
+        du = aligned_empty(h["du"].size, w.du_offset_bytes)
+        du.copy_(torch.from_numpy(h["du"].reshape(-1)))
+        self.du = du.view(h["du"].shape)
+        self.beta = torch.from_numpy(h["beta"]).cuda()
+        self.kpay = torch.from_numpy(h["kpay"]).cuda()
+        self.rec = torch.from_numpy(h["rec"]).cuda()
+        self.bpre = torch.from_numpy(h["bpre"]).cuda() if h["ssr"] < 0 else None
+        self.eff = torch.zeros((h["planes"], w.N * w.n), dtype=torch.float32, device="cuda")
+        self.gout = torch.zeros_like(self.eff)
+        self.args = g.pa2_args(self.grad, self.bank, self.snap, h["ssr"], self.du, self.beta, self.kpay, self.rec,
+                               self.bpre, self.eff, self.gout, w.P, w.C, w.W, w.hd, ld_u=w.ld_u)
+        self.plan = g.sdm_pa2_plan_for(self.args, torch.cuda.get_device_properties(0).multi_processor_count)
+        self.stream = torch.cuda.current_stream()
+        # algorithmic bytes and flops of a pass, from the records: each record (16 bytes) and output (4 bytes per
+        # plane, two outputs) once, the token rows and beta once per chunk, a grad row and a snapshot row read per
+        # valid FIRST, a grad row and a bank row written per valid LAST
+        pay = h["kpay"].view(np.uint32)
+        valid = (pay & np.uint32(0x20000)) == 0
+        vfirst = int(((pay & np.uint32(0x80000000)) != 0)[valid].sum())
+        vlast = int(((pay & np.uint32(0x40000000)) != 0)[valid].sum())
+        recs = w.N * w.n
+        self.bytes_pass = (recs * (16 + 8 * h["planes"]) + w.N * w.C * (w.hd + 1) * 4 +
+                           (vfirst + vlast) * 2 * w.hd * 4)
+        self.flops_pass = recs * w.hd * 4 + (vfirst + vlast) * w.hd * 2 + recs * w.nsl * 2 * 31
+
+    def one_pass(self):
+        self.g.sdm_pa2_steps(self.args, 0, self.w.T, self.g.SDM_GX_STEPS_FORWARD, self.plan, self.stream)
+
+    def reset(self):
+        self.grad.copy_(self.torch.from_numpy(self.h["grad"]))
+        self.bank.copy_(self.torch.from_numpy(self.h["bank"]))
+        self.torch.cuda.synchronize()
+
+    def result(self):
+        self.torch.cuda.synchronize()
+        return self.grad.cpu().numpy(), self.bank.cpu().numpy(), self.eff.cpu().numpy(), self.gout.cpu().numpy()
+
+    def rates(self, ms):
+        s = ms * 1e-3
+        return {"ms_per_pass": ms, "ms_per_step": ms / self.w.T, "gflops": self.flops_pass / s / 1e9,
+                "hbm_gbps": self.bytes_pass / s / 1e9, "frac": self.bytes_pass / s / 1e9 / HBM_PEAK_GBS}
+
+
 def rates(w, ms_per_pass, launches_per_pass):
     bytes_pass, flops_pass = w.T * w.bytes_per_step, w.T * w.flops_per_step
     s = ms_per_pass * 1e-3
@@ -223,6 +287,30 @@ def rates(w, ms_per_pass, launches_per_pass):
             "ms_per_launch": ms_per_pass / launches_per_pass,
             "gflops": flops_pass / s / 1e9, "hbm_gbps": bytes_pass / s / 1e9,
             "frac": bytes_pass / s / 1e9 / HBM_PEAK_GBS}
+
+
+def b_warm(torch, one_pass, stream, passes, warmup):
+    """Milliseconds per pass: `passes` passes back to back between two events on the launch stream."""
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(passes):
+        one_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / passes
+
+
+class pb_cold_shim:
+    """The attributes Bench.cold_ms uses, for a Phase A workload."""
+
+    def __init__(self, pb, torch, flush, sink):
+        self.torch, self.stream, self.flush, self.sink = torch, pb.stream, flush, sink
+
+    def flush_read(self):
+        self.torch.sum(self.flush, dim=0, out=self.sink)
 
 
 def same_bits(np, a, b):
@@ -257,15 +345,31 @@ def main():
         plan_override = g.make_mfma_plan(*f) if engine == "mfma" else g.make_plan(*f)
 
     # ---- profiling runs: the headline launch alone ------------------------------------------------------------------
+    if args.profile and args.phase_a:
+        pb = Pa2Bench(g, torch, args.phase_a)
+        if args.profile == "cold":
+            shim = pb_cold_shim(pb, torch, flush, sink)
+            for _ in range(args.steps):
+                shim.flush_read()
+                pb.one_pass()
+            torch.cuda.synchronize()
+            ms = None
+        else:
+            ms = b_warm(torch, pb.one_pass, pb.stream, args.steps, args.warmup)
+        print(json.dumps({"profile": args.profile, "phase_a": args.phase_a, "passes": args.steps,
+                          "ms_per_pass_warm": ms, "plan": pb.plan.as_dict()}), flush=True)
+        return 0
     if args.profile:
         b = Bench(g, inputs, torch, head, flush, sink)
         step = b.step(plan_override)
         one_pass = b.pass_fn(step, args.driver)
-        if args.profile == "warm":
+        if args.profile == "warm":                      # the benchmark's own launches: back to back from the host
+            ms = b.warm_ms(one_pass, args.steps, args.warmup)
+        elif args.profile == "graph":
             # launches captured in a HIP graph (torch's stream capture of the library's kernel launches), so that the
             # traced dispatches run back to back whatever the profiler's per-launch host cost
             if args.driver == "graph":
-                raise SystemExit("bench.py: --profile warm takes the fused or per-step driver")
+                raise SystemExit("bench.py: --profile graph takes the fused or per-step driver")
             per_graph = 20
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
@@ -372,6 +476,39 @@ def main():
         if key != head.key:
             del b
 
+    # ---- Phase A: the consumer of the updated d_u, per-step launches -------------------------------------------------
+    phase_a = {}
+    if not args.no_phase_a:
+        for key in ("a3", "a5"):
+            pb = Pa2Bench(g, torch, key)
+            e = {"description": pb.w.description, "plan": pb.plan.as_dict(), "kernel": "gx_pa2_kernel",
+                 "algorithmic_bytes_per_pass": pb.bytes_pass, "algorithmic_flops_per_pass": pb.flops_pass}
+            pb.one_pass()
+            got = pb.result()
+            if oracle:
+                h, w = pb.h, pb.w
+                grad, bank = h["grad"].copy(), h["bank"].copy()
+                eff = np.zeros((h["planes"], w.N * w.n), np.float32)
+                gout = eff.copy()
+                t = time.perf_counter()
+                for ti in range(w.T):
+                    oracle.pa2_step(grad, bank, h["snap"], h["ssr"], h["du"], h["beta"], h["rec"], eff, gout, ti,
+                                    w.P, w.C, w.W, w.hd)
+                e["oracle_pass_s"] = time.perf_counter() - t
+                e["bit_exact"] = all(same_bits(np, a, b) for a, b in zip(got, (grad, bank, eff, gout)))
+            else:
+                e["bit_exact"] = None
+            pb.reset()
+            e["warm"] = pb.rates(b_warm(torch, pb.one_pass, pb.stream, max(20, args.steps // 4), 5))
+            pb.reset()
+            e["cold"] = pb.rates(Bench.cold_ms(pb_cold_shim(pb, torch, flush, sink), pb.one_pass)[0])
+            pb.reset()
+            phase_a[key] = e
+            print(f"bench: phase A {key}: warm {e['warm']['ms_per_pass'] * 1e3:.2f} us/pass (frac "
+                  f"{e['warm']['frac']:.3f}), cold {e['cold']['ms_per_pass'] * 1e3:.2f} us/pass (frac "
+                  f"{e['cold']['frac']:.3f}), bit_exact {e['bit_exact']}", file=sys.stderr, flush=True)
+            del pb
+
     # ---- CPU baseline: the oracle on whole passes of the headline workload ---------------------------------------------
     cpu = None
     if oracle:
@@ -447,6 +584,7 @@ def main():
         "cold": headline["cold"],
         "per_step_driver": headline["per_step"],
         "workloads": table,
+        "phase_a": phase_a,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
     }

@@ -17,12 +17,16 @@
 //     rows of d_u (C rows of the pair's columns) and its beta values in LDS once; wavefront w walks tile
 //     cta*WAVES + w: records [snap_back(tile*L), snap_back((tile+1)*L)), tile boundaries moved back to a group's
 //     FIRST through the payload's distance field (the page's snap_back), so every group is walked by one wavefront.
-//   * Records are loaded 64 at a time (lane l: record jb + l) and broadcast with readlane; the 32-lane sums are four
-//     DPP adds (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror) and a ds_swizzle swap of the
-//     16-lane halves. After each xor-butterfly level every lane of an aligned block holds the same block sum, so
-//     pairing a lane with any lane of the partner block (the mirrors) gives the page's tree, bit for bit.
-//   * Per record, lane k of the batch collects the record's values (compare and select), so each batch writes its
-//     outputs with one store per plane.
+//   * Records are loaded 64 at a time (lane l: record jb + l) and broadcast with readlane. The batch is walked in
+//     segments from one FIRST to the next, so a group's grad and snapshot rows stay in the same registers over its
+//     records.
+//   * The 32-lane sums are four DPP adds (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror),
+//     after which every lane of a 16-lane row holds the row's sum, and a row_bcast:15 DPP add that joins the lower
+//     row's sum to the upper row's. After each xor-butterfly level every lane of an aligned block holds the same block
+//     sum, so pairing a lane with any lane of the partner block (the mirrors, the broadcast) gives the page's tree,
+//     bit for bit. The sums are read from lanes 31 and 63.
+//   * Per record, lane k of the batch collects the record's dot values (readlane, compare and select); each FIRST
+//     hands its group's g to the lanes from its own on. Each batch writes its outputs with one store per plane.
 //   * Record fields are bounds-checked before any access they steer (token < C, write < W, slot < slots, snapshot
 //     row < snap_rows): a record outside the definition gives unspecified values but never reaches outside the
 //     buffers.
@@ -48,14 +52,20 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// the balanced pairwise sum over each 32-lane half, in lane order; every lane of the half gets it
+// the balanced pairwise sum over each 32-lane half, in lane order, held by lanes 16-31 and 48-63 (the upper row of
+// each half; the lower rows hold their own 16-lane sums)
 __device__ __forceinline__ float tree32(float v) {
     v = v + dpp<0xB1>(v);          // quad_perm [1,0,3,2]: lanes l, l^1
     v = v + dpp<0x4E>(v);          // quad_perm [2,3,0,1]: 2-blocks
     v = v + dpp<0x141>(v);         // row_half_mirror: 4-blocks of an 8-lane half row
     v = v + dpp<0x140>(v);         // row_mirror: 8-blocks of a 16-lane row
-    v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));   // 16-blocks
-    return v;
+    // row_bcast:15 into rows 1 and 3: the lower row's sum (its lane 15) joins the upper row's (16-blocks)
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF,
+                                                                     false));
+}
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 // fmul then three fmaf over a lane's 4 columns
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
     const int64_t srow_base = a.ssr < 0 ? chunk * n : static_cast<int64_t>(a.ti) * a.ssr + static_cast<int64_t>(p) * n;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gdw = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
-    float g = 0.f;                                     // the group's dot(gdw, sn), per half
+    float g = 0.f;                                     // the group's dot(gdw, sn): lanes 16-31 slice A, 48-63 slice B
     const int64_t obase = chunk * n;
     for (int jb = s; jb < e; jb += 64) {
         const int nrec = e - jb < 64 ? e - jb : 64;
@@ -176,56 +186,71 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
             r2 = q.z;
             r3 = q.w;
         }
-        float effA = 0.f, effB = 0.f, gA = 0.f, gB = 0.f;
-        for (int k = 0; k < nrec; ++k) {
-            const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
-            int tok = static_cast<int>((pay >> 9) & 0xFFu);
-            tok = tok < C ? tok : C - 1;
-            const float sck = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r2, k));
-            f32x4 x = tok_s[tok * 32 * SG + tl];
-            if (!on) x = f32x4{0.f, 0.f, 0.f, 0.f};
-            const bool valid = !(pay & kInvalid);
-            if (pay & kFirst) {
+        // The batch is needed at once. Waiting for it here, outside the record loop, keeps the compiler from placing
+        // that wait at the loop's head, where it would also wait for every store of the records before.
+        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+        const uint64_t fm = __ballot(lane < nrec && (static_cast<uint32_t>(r0) & kFirst));   // the batch's FIRSTs
+        // Lane l collects record jb + l's dot values and its group's g (the group open at the batch start for the
+        // records before the batch's first FIRST; each FIRST takes over the lanes from its own on).
+        float effA = 0.f, effB = 0.f;
+        float gA = lane_value(g, 31), gB = lane_value(g, 63);
+        // segments: from a FIRST (or the batch start) to the record before the next FIRST (or the batch end), so the
+        // group's rows stay in the same registers over its records
+        for (int k = 0; k < nrec;) {
+            if ((fm >> k) & 1) {
+                const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
                 acc = f32x4{0.f, 0.f, 0.f, 0.f};
                 gdw = f32x4{0.f, 0.f, 0.f, 0.f};
                 sn = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (valid) {
+                if (!(pay & kInvalid)) {
                     const int64_t slot = __builtin_amdgcn_readlane(r1, k);
                     const int64_t srow = a.ssr < 0 ? srow_base + gw
-                                                   : srow_base + static_cast<int64_t>(tok) * W + (pay & 0xFFu);
+                                                   : srow_base + static_cast<int64_t>((pay >> 9) & 0xFFu) * W +
+                                                         (pay & 0xFFu);
                     ++gw;
                     if (on && slot >= 0 && slot < a.slots) gdw = load_cols(a.grad + slot * hd + col0, nv);
                     if (on && srow < a.snap_rows) sn = load_cols(a.snap + srow * hd + col0, nv);
                 }
                 g = tree32(dot4(gdw, sn));
-            }
-            acc.x = __builtin_fmaf(sck, x.x, acc.x);
-            acc.y = __builtin_fmaf(sck, x.y, acc.y);
-            acc.z = __builtin_fmaf(sck, x.z, acc.z);
-            acc.w = __builtin_fmaf(sck, x.w, acc.w);
-            const float dot = tree32(dot4(x, sn));
-            if ((pay & kLast) && valid) {
-                const int64_t slot = __builtin_amdgcn_readlane(r1, k);
-                const float cpe = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r3, k));
-                if (on && slot >= 0 && slot < a.slots) {
-                    f32x4 o;
-                    o.x = __builtin_fmaf(gdw.x, cpe, acc.x);
-                    o.y = __builtin_fmaf(gdw.y, cpe, acc.y);
-                    o.z = __builtin_fmaf(gdw.z, cpe, acc.z);
-                    o.w = __builtin_fmaf(gdw.w, cpe, acc.w);
-                    store_cols(a.grad + slot * hd + col0, o, nv);
-                    store_cols(a.bank + slot * hd + col0, sn, nv);
+                const float g0 = lane_value(g, 31), g1 = lane_value(g, 63);
+                if (lane >= k) {
+                    gA = g0;
+                    gB = g1;
                 }
             }
-            const float dA = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dot), 0));
-            const float dB = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dot), 32));
-            const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 0));
-            const float g1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 32));
-            if (lane == k) {
-                effA = dA;
-                effB = dB;
-                gA = g0;
-                gB = g1;
+            const uint64_t later = k >= 63 ? 0ull : fm & (~0ull << (k + 1));
+            const int kend = later ? static_cast<int>(__builtin_ctzll(later)) : nrec;
+            for (; k < kend; ++k) {
+                const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
+                int tok = static_cast<int>((pay >> 9) & 0xFFu);
+                tok = tok < C ? tok : C - 1;
+                const float sck = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r2, k));
+                // +0 for lanes off the head (staged so); with one slice per wavefront, lanes 32-63 read lanes 0-31's
+                // entries and their results are never used
+                const f32x4 x = tok_s[tok * 32 * SG + tl];
+                acc.x = __builtin_fmaf(sck, x.x, acc.x);
+                acc.y = __builtin_fmaf(sck, x.y, acc.y);
+                acc.z = __builtin_fmaf(sck, x.z, acc.z);
+                acc.w = __builtin_fmaf(sck, x.w, acc.w);
+                const float dot = tree32(dot4(x, sn));
+                if ((pay & kLast) && !(pay & kInvalid)) {
+                    const int64_t slot = __builtin_amdgcn_readlane(r1, k);
+                    const float cpe = __builtin_bit_cast(float, __builtin_amdgcn_readlane(r3, k));
+                    if (on && slot >= 0 && slot < a.slots) {
+                        f32x4 o;
+                        o.x = __builtin_fmaf(gdw.x, cpe, acc.x);
+                        o.y = __builtin_fmaf(gdw.y, cpe, acc.y);
+                        o.z = __builtin_fmaf(gdw.z, cpe, acc.z);
+                        o.w = __builtin_fmaf(gdw.w, cpe, acc.w);
+                        store_cols(a.grad + slot * hd + col0, o, nv);
+                        store_cols(a.bank + slot * hd + col0, sn, nv);
+                    }
+                }
+                const float dA = lane_value(dot, 31), dB = lane_value(dot, 63);
+                if (lane == k) {
+                    effA = dA;
+                    effB = dB;
+                }
             }
         }
         // outputs of records jb .. jb + nrec - 1 (lane l: record jb + l)

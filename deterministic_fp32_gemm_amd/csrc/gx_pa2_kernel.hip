@@ -43,6 +43,7 @@ constexpr uint32_t kLast = 0x40000000u;
 constexpr uint32_t kInvalid = 0x00020000u;
 constexpr int kDistShift = 18;
 constexpr uint32_t kDistMax = 4095u;
+constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, untyped dword access
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
@@ -101,6 +102,14 @@ __device__ __forceinline__ void store_cols(float* p, f32x4 v, int nv) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 16 bytes at byte offset voff of row `row` of a [rows][hd] array, through a buffer resource of `cols` columns from
+// the row's start (0: an empty range). Every dword past the range reads +0 and touches no memory.
+__device__ __forceinline__ f32x4 row_load(const float* base, int64_t row, int cols, int hd, int voff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base) + row * hd, (short)0,
+                                                                       cols * 4, kBufferFlags);
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
 
 // The FIRST position of the group holding position j (0 for j <= 0, n for j >= n): the payload's distance field, or
 // for distances of kDistMax and more a scan back 64 records at a time. Wavefront-uniform.
@@ -174,7 +183,9 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
     const int64_t srow_base = a.ssr < 0 ? chunk * n : static_cast<int64_t>(a.ti) * a.ssr + static_cast<int64_t>(p) * n;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gdw = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
+    f32x4 pg = {0.f, 0.f, 0.f, 0.f}, ps = {0.f, 0.f, 0.f, 0.f};   // the next group's grad and snapshot columns
     float g = 0.f;                                     // the group's dot(gdw, sn): lanes 16-31 slice A, 48-63 slice B
+    const int voff = on ? col0 * 4 : 0x7FFFFFF0;       // this lane's byte offset in a row; past any row when off
     const int64_t obase = chunk * n;
     for (int jb = s; jb < e; jb += 64) {
         const int nrec = e - jb < 64 ? e - jb : 64;
@@ -194,33 +205,9 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
         // records before the batch's first FIRST; each FIRST takes over the lanes from its own on).
         float effA = 0.f, effB = 0.f;
         float gA = lane_value(g, 31), gB = lane_value(g, 63);
-        // segments: from a FIRST (or the batch start) to the record before the next FIRST (or the batch end), so the
-        // group's rows stay in the same registers over its records
-        for (int k = 0; k < nrec;) {
-            if ((fm >> k) & 1) {
-                const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
-                acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                gdw = f32x4{0.f, 0.f, 0.f, 0.f};
-                sn = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (!(pay & kInvalid)) {
-                    const int64_t slot = __builtin_amdgcn_readlane(r1, k);
-                    const int64_t srow = a.ssr < 0 ? srow_base + gw
-                                                   : srow_base + static_cast<int64_t>((pay >> 9) & 0xFFu) * W +
-                                                         (pay & 0xFFu);
-                    ++gw;
-                    if (on && slot >= 0 && slot < a.slots) gdw = load_cols(a.grad + slot * hd + col0, nv);
-                    if (on && srow < a.snap_rows) sn = load_cols(a.snap + srow * hd + col0, nv);
-                }
-                g = tree32(dot4(gdw, sn));
-                const float g0 = lane_value(g, 31), g1 = lane_value(g, 63);
-                if (lane >= k) {
-                    gA = g0;
-                    gB = g1;
-                }
-            }
-            const uint64_t later = k >= 63 ? 0ull : fm & (~0ull << (k + 1));
-            const int kend = later ? static_cast<int>(__builtin_ctzll(later)) : nrec;
-            for (; k < kend; ++k) {
+        // the records k0 .. k1 - 1 of one group
+        auto walk = [&](int k0, int k1) {
+            for (int k = k0; k < k1; ++k) {
                 const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
                 int tok = static_cast<int>((pay >> 9) & 0xFFu);
                 tok = tok < C ? tok : C - 1;
@@ -252,6 +239,45 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
                     effB = dB;
                 }
             }
+        };
+        // The rows a FIRST record opens its group with are loaded one group ahead: at the batch start those of its
+        // first FIRST, at each FIRST those of the next one, while the group is walked. Each row is read through a
+        // buffer resource spanning its hd columns (none for an INVALID record or a row out of range), so lanes past
+        // the head or the row's end, and records without rows, read +0 with no branch, and the loads are unconditional.
+        auto fetch = [&](int k2) {                     // the rows of the batch's FIRST record k2 (k2 >= nrec: none)
+            bool use = false;
+            int64_t slot = 0, srow = 0;
+            if (k2 < nrec) {
+                const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k2));
+                use = !(pay & kInvalid);
+                slot = __builtin_amdgcn_readlane(r1, k2);
+                srow = a.ssr < 0 ? srow_base + gw
+                                 : srow_base + static_cast<int64_t>((pay >> 9) & 0xFFu) * W + (pay & 0xFFu);
+            }
+            const bool gok = use && slot >= 0 && slot < a.slots, sok = use && srow >= 0 && srow < a.snap_rows;
+            pg = row_load(a.grad, gok ? slot : 0, gok ? hd : 0, hd, voff);
+            ps = row_load(a.snap, sok ? srow : 0, sok ? hd : 0, hd, voff);
+        };
+        const int kf = fm ? static_cast<int>(__builtin_ctzll(fm)) : nrec;
+        fetch(kf);
+        walk(0, kf);                                   // the group open at the batch start
+        for (int k = kf; k < nrec;) {                  // from each FIRST to the record before the next one
+            const uint32_t pay = static_cast<uint32_t>(__builtin_amdgcn_readlane(r0, k));
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            gdw = pg;
+            sn = ps;
+            if (!(pay & kInvalid)) ++gw;
+            const uint64_t later = k >= 63 ? 0ull : fm & (~0ull << (k + 1));
+            const int kend = later ? static_cast<int>(__builtin_ctzll(later)) : nrec;
+            fetch(kend);
+            g = tree32(dot4(gdw, sn));
+            const float g0 = lane_value(g, 31), g1 = lane_value(g, 63);
+            if (lane >= k) {
+                gA = g0;
+                gB = g1;
+            }
+            walk(k, kend);
+            k = kend;
         }
         // outputs of records jb .. jb + nrec - 1 (lane l: record jb + l)
         if (lane < nrec) {

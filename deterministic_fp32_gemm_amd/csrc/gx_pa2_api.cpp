@@ -21,7 +21,7 @@ int record_hip_error(hipError_t e);     // gx_gemm_api.cpp: keeps e for sdm_gx_l
 namespace {
 
 constexpr int kTargetWavesPerCu = 32;    // 8 per SIMD: gathers at group starts are latency-bound
-constexpr int kMinTile = 8;
+constexpr int kMinTile = 4;     // records per tile at least (4 measured 8% faster than 8 on 64 x 8-record chunks)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

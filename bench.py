@@ -320,7 +320,7 @@ def same_bits(np, a, b):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the update shards over "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the update shards over "
               "chunks with no exchange, so N GPUs would run N independent copies of this benchmark", file=sys.stderr)
         return 2
     import numpy as np

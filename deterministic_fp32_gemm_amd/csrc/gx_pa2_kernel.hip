@@ -111,12 +111,13 @@ __device__ __forceinline__ f32x4 row_load(const float* base, int64_t row, int co
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-// The FIRST position of the group holding position j (0 for j <= 0, n for j >= n): the payload's distance field, or
-// for distances of kDistMax and more a scan back 64 records at a time. Wavefront-uniform.
-__device__ __forceinline__ int snap_back(const int32_t* kp, int j, int n, int lane) {
+
+// The FIRST position of the group holding position j (0 for j <= 0, n for j >= n), from p = the payload at j (any
+// value where j <= 0 or j >= n): the payload's distance field, or for distances of kDistMax and more a scan back 64
+// records at a time. Wavefront-uniform.
+__device__ __forceinline__ int snap_back(const int32_t* kp, int j, int n, int lane, uint32_t p) {
     if (j <= 0) return 0;
     if (j >= n) return n;
-    const uint32_t p = static_cast<uint32_t>(uniform(kp[j]));
     if (p & kFirst) return j;
     const uint32_t d = (p >> kDistShift) & kDistMax;
     if (d < kDistMax) return j - static_cast<int>(d);
@@ -152,34 +153,67 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
     const int nv = on ? (hd - col0 < 4 ? hd - col0 : 4) : 0;
     const int tl = SG == 2 ? lane : hl;                // this lane's entry of a token row in LDS
 
-    // stage the chunk's token rows (the pair's columns, +0 past the slice or the head) and beta
+    // Set-up loads in three round trips: (1) the first token rows, beta and the payloads at both tile ends; (2) the
+    // snapshot ordinal's block prefix and payloads, and the tile's first record batch, in flight across the staging
+    // barrier; (3) after it, the first group's rows.
     const float* rows = a.du + chunk * C * a.ld_u;
-    for (int t = wave; t < C; t += WAVES) {
-        const f32x4 v = on ? load_cols(rows + static_cast<int64_t>(t) * a.ld_u + col0, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
-        if (SG == 2 || half == 0) tok_s[t * 32 * SG + tl] = v;
-    }
-    for (int i = static_cast<int>(threadIdx.x); i < C; i += 64 * WAVES) beta_s[i] = a.beta[chunk * C + i];
-    __syncthreads();
-
     const int32_t* kp = a.kpay + chunk * n;
     const int32_t* rp = a.rec + chunk * n * 4;
     const int tile = cta * WAVES + wave;
     const int64_t t0 = static_cast<int64_t>(tile) * a.L;
-    const int s = snap_back(kp, t0 < n ? static_cast<int>(t0) : n, n, lane);
-    const int e = snap_back(kp, t0 + a.L < n ? static_cast<int>(t0 + a.L) : n, n, lane);
-    if (s >= e) return;                                // no barrier follows
-
-    // dense snapshot rows: the ordinal of the tile's first valid FIRST (block prefix + valid FIRSTs in the block
-    // before s)
-    int gw = 0;
-    if (a.ssr < 0) {
-        const int bs = s >> 5;
-        const int q = 32 * bs + lane;
-        const uint32_t pq = (lane < 32 && q < s) ? static_cast<uint32_t>(kp[q]) : 0u;
-        gw = a.bpre[chunk * ((n + 31) / 32 + 1) + bs] +
-             static_cast<int>(__builtin_popcountll(__ballot((pq & kFirst) && !(pq & kInvalid))));
-        gw = uniform(gw);
+    const int j0 = t0 < n ? static_cast<int>(t0) : n, j1 = t0 + a.L < n ? static_cast<int>(t0 + a.L) : n;
+    f32x4 v0[4];                                       // this wavefront's first 4 token rows (rows wave + u * WAVES)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = wave + u * WAVES;
+        v0[u] = on && t < C ? load_cols(rows + static_cast<int64_t>(t) * a.ld_u + col0, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const int bi = static_cast<int>(threadIdx.x);      // beta of token bi (C <= 256 <= the workgroup's threads)
+    const float bv = bi < C ? a.beta[chunk * C + bi] : 0.f;
+    // both payloads in flight at once (clamped reads, no branch: n >= 1)
+    const int32_t q0 = kp[j0 < n ? j0 : n - 1], q1 = kp[j1 < n ? j1 : n - 1];
+    const uint32_t p0 = static_cast<uint32_t>(uniform(q0)), p1 = static_cast<uint32_t>(uniform(q1));
+    const int s = snap_back(kp, j0, n, lane, p0);
+    const int e = snap_back(kp, j1, n, lane, p1);
+    // stage the chunk's token rows (the pair's columns, +0 past the slice or the head) and beta
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = wave + u * WAVES;
+        if (t < C && (SG == 2 || half == 0)) tok_s[t * 32 * SG + tl] = v0[u];
+    }
+    if (bi < C) beta_s[bi] = bv;
+    // dense snapshot rows: the ordinal of the tile's first valid FIRST is the block prefix plus the valid FIRSTs in
+    // the block before s
+    int bp = 0;
+    uint32_t pq = 0u;                                  // payload of record 32 * (s / 32) + lane (masked at use)
+    const bool before_s = lane < 32 && 32 * (s >> 5) + lane < s;
+    if (a.ssr < 0 && s < e) {                          // (clamped read: s < n; bs <= n / 32)
+        const int bs = s >> 5;
+        pq = static_cast<uint32_t>(kp[before_s ? 32 * bs + lane : s]);
+        bp = a.bpre[chunk * ((n + 31) / 32 + 1) + bs];
+    }
+    // records jb .. jb + 63 (lane l: record jb + l; 16-byte records, 16-byte aligned: checked on the host). Lanes
+    // past the batch (jb + l >= e) read record jb again, a clamped read with no branch; every use of a batch lane is
+    // for records below e, so nothing waits for the load until the walk needs it.
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    auto load_batch = [&](int jb) {
+        const int4 q = reinterpret_cast<const int4*>(rp)[jb + lane < e ? jb + lane : jb];
+        r0 = q.x;
+        r1 = q.y;
+        r2 = q.z;
+        r3 = q.w;
+    };
+    if (s < e) load_batch(s);
+    for (int t = wave + 4 * WAVES; t < C; t += WAVES) {   // the rest of the token rows (C > 4 * WAVES)
+        const f32x4 v = on ? load_cols(rows + static_cast<int64_t>(t) * a.ld_u + col0, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (SG == 2 || half == 0) tok_s[t * 32 * SG + tl] = v;
+    }
+    __syncthreads();
+    if (s >= e) return;                                // no barrier follows
+    asm volatile("" : "+v"(pq));                       // the ordinal's payload is examined here, not at its load
+    int gw = 0;
+    if (a.ssr < 0)
+        gw = uniform(bp + static_cast<int>(__builtin_popcountll(__ballot(before_s && (pq & kFirst) && !(pq & kInvalid)))));
     const int64_t srow_base = a.ssr < 0 ? chunk * n : static_cast<int64_t>(a.ti) * a.ssr + static_cast<int64_t>(p) * n;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gdw = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
@@ -189,14 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
     const int64_t obase = chunk * n;
     for (int jb = s; jb < e; jb += 64) {
         const int nrec = e - jb < 64 ? e - jb : 64;
-        int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-        if (lane < nrec) {                             // 16-byte records, 16-byte aligned (checked on the host)
-            const int4 q = reinterpret_cast<const int4*>(rp)[jb + lane];
-            r0 = q.x;
-            r1 = q.y;
-            r2 = q.z;
-            r3 = q.w;
-        }
+        if (jb != s) load_batch(jb);
         // The batch is needed at once. Waiting for it here, outside the record loop, keeps the compiler from placing
         // that wait at the loop's head, where it would also wait for every store of the records before.
         __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)

@@ -20,6 +20,12 @@
 //   * Records are loaded 64 at a time (lane l: record jb + l) and broadcast with readlane. The batch is walked in
 //     segments from one FIRST to the next, so a group's grad and snapshot rows stay in the same registers over its
 //     records.
+//   * A group's grad and snapshot rows are loaded one group ahead (at a batch's start those of its first FIRST, at
+//     each FIRST those of the next) through a buffer resource per row, whose range is the row, or empty for an
+//     INVALID record or a row index out of range: the loads need no branch and land in fixed registers.
+//   * A tile's set-up takes three memory round trips: the first token rows, beta and the payloads at the tile's ends;
+//     the snapshot ordinal's inputs and the first record batch, in flight across the staging barrier; the first
+//     group's rows.
 //   * The 32-lane sums are four DPP adds (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror),
 //     after which every lane of a 16-lane row holds the row's sum, and a row_bcast:15 DPP add that joins the lower
 //     row's sum to the upper row's. After each xor-butterfly level every lane of an aligned block holds the same block

@@ -20,10 +20,11 @@ struct Pa2Args {
     float* out_g;
     int64_t slots, snap_rows, ssr, ld_u, plane;
     int32_t ti, P, C, W, n, hd, nsl, slw, npair, ctas, L;
+    int32_t stage_out;      // 1: outputs gathered in LDS and written out by the workgroup's last wavefront
 };
 
-// The kernel instance for (slices per wavefront, wavefronts per workgroup), or nullptr. Launched with 64 * waves
-// threads, lds bytes of dynamic LDS, one Pa2Args argument by value.
-const void* find_pa2_kernel(int slices_per_wave, int waves);
+// The kernel instance for (slices per wavefront, wavefronts per workgroup, outputs staged in LDS), or nullptr.
+// Launched with 64 * waves threads, lds bytes of dynamic LDS, one Pa2Args argument by value (stage_out == staged).
+const void* find_pa2_kernel(int slices_per_wave, int waves, bool staged);
 
 }  // namespace sdm_gx

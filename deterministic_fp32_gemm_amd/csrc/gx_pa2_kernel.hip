@@ -32,7 +32,11 @@
 //     sum, so pairing a lane with any lane of the partner block (the mirrors, the broadcast) gives the page's tree,
 //     bit for bit. The sums are read from lanes 31 and 63.
 //   * Per record, lane k of the batch collects the record's dot values (readlane, compare and select); each FIRST
-//     hands its group's g to the lanes from its own on. Each batch writes its outputs with one store per plane.
+//     hands its group's g to the lanes from its own on. Each batch writes its outputs with one store per plane,
+//     scattered over the chunk (entry t*W + w); when one workgroup covers the chunk they go to LDS instead, and the
+//     workgroup's last wavefront to finish (an LDS count) writes each output plane of the chunk in one contiguous run.
+//     That instance is capped at 80 SGPRs, so that a SIMD holds 8 of its wavefronts and a CU's two workgroups run
+//     from the start.
 //   * Record fields are bounds-checked before any access they steer (token < C, write < W, slot < slots, snapshot
 //     row < snap_rows): a record outside the definition gives unspecified values but never reaches outside the
 //     buffers.
@@ -138,10 +142,15 @@ __device__ __forceinline__ int snap_back(const int32_t* kp, int j, int n, int la
     }
 }
 
-template <int SG, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
-    extern __shared__ f32x4 tok_s[];                   // [C][32 * SG] token rows, then beta [C]
+// The step for one workgroup. STG: outputs staged in LDS and written out whole at the end; else one store per record
+// and plane.
+template <int SG, int WAVES, bool STG>
+__device__ __forceinline__ void pa2_workgroup(const Pa2Args& a) {
+    extern __shared__ f32x4 tok_s[];                   // [C][32 * SG] token rows, beta [C], then (stage_out) the
+                                                       // finished-wavefront count and the outputs [np][n]
     float* const beta_s = reinterpret_cast<float*>(tok_s + a.C * 32 * SG);
+    uint32_t* const done_s = reinterpret_cast<uint32_t*>(beta_s + a.C);
+    float* const out_s = beta_s + a.C + 1;
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
     const int half = lane >> 5, hl = lane & 31;
@@ -158,6 +167,8 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
     const bool on = lane_slice && 4 * hl < a.slw && col0 < hd;
     const int nv = on ? (hd - col0 < 4 ? hd - col0 : 4) : 0;
     const int tl = SG == 2 ? lane : hl;                // this lane's entry of a token row in LDS
+    const int s0 = sp * SG;                            // the workgroup's first slice
+    const bool two = a.nsl > 1 && SG == 2 && s0 + 1 < a.nsl;   // outputs of a second slice (planes 2 and 3)
 
     // Set-up loads in three round trips: (1) the first token rows, beta and the payloads at both tile ends; (2) the
     // snapshot ordinal's block prefix and payloads, and the tile's first record batch, in flight across the staging
@@ -188,6 +199,10 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
         if (t < C && (SG == 2 || half == 0)) tok_s[t * 32 * SG + tl] = v0[u];
     }
     if (bi < C) beta_s[bi] = bv;
+    if (STG) {                                         // +0 in every staged output, the count at 0
+        for (int i = bi; i < (two ? 4 : 2) * n; i += 64 * WAVES) out_s[i] = 0.f;
+        if (bi == 0) *done_s = 0u;
+    }
     // dense snapshot rows: the ordinal of the tile's first valid FIRST is the block prefix plus the valid FIRSTs in
     // the block before s
     int bp = 0;
@@ -215,7 +230,31 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
         if (SG == 2 || half == 0) tok_s[t * 32 * SG + tl] = v;
     }
     __syncthreads();
-    if (s >= e) return;                                // no barrier follows
+    // With staged outputs each wavefront counts itself done once its LDS output writes have completed; the last one
+    // of the workgroup then writes the chunk's outputs out, each plane in one contiguous run.
+    auto arrive = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): this wavefront's output writes are in LDS
+        uint32_t prev = 0u;
+        if (lane == 0) prev = __hip_atomic_fetch_add(done_s, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev), 0)) != WAVES - 1) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int64_t ob = chunk * n;
+        float* const e0 = a.out_eff + (a.nsl == 1 ? 0 : s0 * a.plane) + ob;
+        float* const g0 = a.out_g + (a.nsl == 1 ? 0 : s0 * a.plane) + ob;
+        for (int i = lane; i < n; i += 64) {
+            e0[i] = out_s[i];
+            g0[i] = out_s[n + i];
+        }
+        if (two)
+            for (int i = lane; i < n; i += 64) {
+                e0[a.plane + i] = out_s[2 * n + i];
+                g0[a.plane + i] = out_s[3 * n + i];
+            }
+    };
+    if (s >= e) {                                      // no barrier follows
+        if (STG) arrive();
+        return;
+    }
     asm volatile("" : "+v"(pq));                       // the ordinal's payload is examined here, not at its load
     int gw = 0;
     if (a.ssr < 0)
@@ -319,14 +358,21 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
             if (tok < C && w < W) {
                 const bool valid = !(pay & kInvalid);
                 const int64_t o = obase + static_cast<int64_t>(tok) * W + w;
-                if (a.nsl == 1) {
+                const int so = tok * W + w;
+                if (STG) {
+                    out_s[so] = valid ? (a.nsl == 1 ? (-beta_s[tok]) * effA : effA) : 0.f;
+                    out_s[n + so] = valid ? (a.nsl == 1 ? __builtin_bit_cast(float, r3) * gA : gA) : 0.f;
+                    if (two) {
+                        out_s[2 * n + so] = valid ? effB : 0.f;
+                        out_s[3 * n + so] = valid ? gB : 0.f;
+                    }
+                } else if (a.nsl == 1) {
                     a.out_eff[o] = valid ? (-beta_s[tok]) * effA : 0.f;
                     a.out_g[o] = valid ? __builtin_bit_cast(float, r3) * gA : 0.f;
                 } else {
-                    const int s0 = sp * SG;
                     a.out_eff[s0 * a.plane + o] = valid ? effA : 0.f;
                     a.out_g[s0 * a.plane + o] = valid ? gA : 0.f;
-                    if (SG == 2 && s0 + 1 < a.nsl) {
+                    if (two) {
                         a.out_eff[(s0 + 1) * a.plane + o] = valid ? effB : 0.f;
                         a.out_g[(s0 + 1) * a.plane + o] = valid ? gB : 0.f;
                     }
@@ -334,13 +380,29 @@ __global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
             }
         }
     }
+    if (STG) arrive();
+}
+
+template <int SG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gx_pa2_kernel(const Pa2Args a) {
+    pa2_workgroup<SG, WAVES, false>(a);
+}
+
+// With every output plane of a chunk in LDS, 80 SGPRs (some spilled to VGPR lanes) let a SIMD hold 8 of these
+// wavefronts, so both workgroups of a CU run from the start; at 90 and more it holds 7.
+template <int SG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_num_sgpr(80))) void gx_pa2_staged_kernel(
+    const Pa2Args a) {
+    pa2_workgroup<SG, WAVES, true>(a);
 }
 
 }  // namespace
 
-const void* find_pa2_kernel(int slices_per_wave, int waves) {
-#define SDM_PA2_K(SG, WV) \
-    if (slices_per_wave == SG && waves == WV) return reinterpret_cast<const void*>(&gx_pa2_kernel<SG, WV>);
+const void* find_pa2_kernel(int slices_per_wave, int waves, bool staged) {
+#define SDM_PA2_K(SG, WV)                                                                                  \
+    if (slices_per_wave == SG && waves == WV)                                                              \
+        return staged ? reinterpret_cast<const void*>(&gx_pa2_staged_kernel<SG, WV>)                       \
+                      : reinterpret_cast<const void*>(&gx_pa2_kernel<SG, WV>);
     SDM_PA2_K(1, 4) SDM_PA2_K(1, 8) SDM_PA2_K(1, 16) SDM_PA2_K(2, 4) SDM_PA2_K(2, 8) SDM_PA2_K(2, 16)
 #undef SDM_PA2_K
     return nullptr;

@@ -25,9 +25,9 @@
  * Contract on the records (device data the library does not read on the host): each chunk's n records name every
  * (t < C, w < W) pair once; kpay[k][j] equals record j's payload and bpre the counts above; a group's FIRST and LAST
  * name the same slot and no two groups of one step read or write the same grad or bank row (steps are sequential:
- * a step may read rows an earlier step wrote). Records outside the contract give unspecified values in the rows and
- * outputs they name, never an access outside the buffers: the kernel checks every token, write, slot and snapshot
- * row before the access it steers.
+ * a step may read rows an earlier step wrote). Records outside the contract give unspecified values in the rows they
+ * name and in their chunk's outputs, never an access outside the buffers: the kernel checks every token, write, slot
+ * and snapshot row before the access it steers.
  *
  * Memory (caller-owned device memory of the current device; float32 unless marked):
  *   grad, bank   [slots][hd]                 read (grad, at FIRST) and written (both, at LAST) in place
@@ -73,7 +73,9 @@ typedef struct sdm_pa2_args {
 /* How a step is launched (never changes results): slices_per_wave 2 puts two slices in one wavefront (lanes 0-31 and
  * 32-63; the planner's choice when nsl >= 2 and C <= 128), 1 one slice; waves_per_wg 4, 8 or 16 wavefronts per
  * workgroup, which stages a chunk's token rows once; tile_len records per wavefront tile (tiles move back to group
- * starts). Outputs: ctas, npair (slice groups), grid, lds_bytes. */
+ * starts). Outputs: ctas, npair (slice groups), grid, lds_bytes. When one workgroup covers a chunk (ctas == 1) and
+ * the chunk's outputs add at most a quarter to its LDS, it gathers them in LDS and writes each output plane of the
+ * chunk in one contiguous run; lds_bytes then includes them. */
 typedef struct sdm_pa2_plan {
     int32_t slices_per_wave;
     int32_t waves_per_wg;

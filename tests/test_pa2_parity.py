@@ -144,6 +144,21 @@ def test_every_plan_gives_the_same_bits():
     assert n == 42
 
 
+
+@pytest.mark.parametrize("mode", ["forward", "reverse"])
+def test_gathered_outputs_over_steps(mode):
+    """Outputs gathered in LDS (one workgroup per chunk, two slices, d_u rows off a 16-byte boundary), over three
+    steps in either order; the outputs of the chunks a step does not cover keep their bytes."""
+    w = PI.Pa2Workload("gather", 3, 2, 16, 8, 256, 260, 4, 256, False, 3.0, 0.05, "gather")
+    c = Pa2Case(w, "special", seed=5)
+    # 16 tiles of 8 records: one workgroup holds each chunk; its 4 output planes (2 KiB) add an eighth to the 16 KiB
+    # of token rows, so they are gathered in LDS
+    plan = g.make_pa2_plan(2, 16, 8)
+    say(f"phase A gathered outputs {mode}")
+    order = range(w.T) if mode == "forward" else reversed(range(w.T))
+    g.sdm_pa2_steps(c.args, 0, w.T, g.SDM_GX_STEPS_FORWARD if mode == "forward" else g.SDM_GX_STEPS_REVERSE, plan)
+    assert_same(c.result(), c.expect(order), f"gathered outputs {mode}")
+
 def test_planner_plans():
     for key, sg in (("a1", 1), ("a3", 1), ("a5", 2)):
         w = PI.PA2_WORKLOADS[key]

@@ -72,6 +72,72 @@ int main(void) {
                     g.sdm_gx_plan_t.mf_stream_du.offset, g.sdm_gx_plan_t.mf_aln.offset]
 
 
+
+def test_phase_a_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout_pa2.c"
+    fields_a = [f for f, _ in B.sdm_pa2_args_t._fields_]
+    fields_p = [f for f, _ in B.sdm_pa2_plan_t._fields_]
+    body = " ".join(f'printf("%zu ", offsetof(sdm_pa2_args_t, {f}));' for f in fields_a)
+    body += " ".join(f'printf("%zu ", offsetof(sdm_pa2_plan_t, {f}));' for f in fields_p)
+    src.write_text(f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "sdm_gx_pa2.h"
+int main(void) {{
+  printf("%zu %zu ", sizeof(sdm_pa2_args_t), sizeof(sdm_pa2_plan_t));
+  {body}
+  return 0;
+}}
+""")
+    exe = tmp_path / "layout_pa2"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(B.sdm_pa2_args_t), ctypes.sizeof(B.sdm_pa2_plan_t)]
+    want += [getattr(B.sdm_pa2_args_t, f).offset for f in fields_a] + [getattr(B.sdm_pa2_plan_t, f).offset for f in fields_p]
+    assert vals == want
+
+
+def test_c_program_links_and_calls_the_host_entry_points(tmp_path):
+    """A plain C program, linked against the library, calls the entry points that need no device: the ABI version,
+    the argument checks and both planners, with made-up device addresses (nothing is dereferenced)."""
+    src = tmp_path / "use.c"
+    src.write_text(r"""
+#include <stdint.h>
+#include <stdio.h>
+#include "sdm_gx_gemm.h"
+#include "sdm_gx_pa2.h"
+int main(void) {
+  float* du = (float*)(uintptr_t)(1ull << 32);
+  const float* x = (const float*)(uintptr_t)(2ull << 32);
+  const float* dv = (const float*)(uintptr_t)(3ull << 32);
+  sdm_gx_plan_t plan;
+  int ok = sdm_gx_check(du, 260, x, dv, 260, 1024, 1, 512, 64, 256);
+  int bad = sdm_gx_check(du, 255, x, dv, 260, 1024, 1, 512, 64, 256);
+  int pl = sdm_gx_plan_for(512, 64, 256, 260, 260, 0, 4, -1, 256, 160 * 1024, &plan);
+  sdm_pa2_args_t a = {0};
+  a.grad = (float*)(uintptr_t)(4ull << 32); a.bank = (float*)(uintptr_t)(5ull << 32); a.slots = 1 << 17;
+  a.snap = (const float*)(uintptr_t)(6ull << 32); a.snap_rows = 2 * 512 * 512; a.ssr = 512 * 512;
+  a.d_u = x; a.ld_u = 260; a.beta = (const float*)(uintptr_t)(7ull << 32);
+  a.kpay = (const int32_t*)(uintptr_t)(8ull << 32); a.rec = (const int32_t*)(uintptr_t)(9ull << 32);
+  a.out_eff = (float*)(uintptr_t)(10ull << 32); a.out_g = (float*)(uintptr_t)(11ull << 32);
+  a.N = 1024; a.P = 512; a.C = 64; a.W = 8; a.hd = 256; a.planes = 2; a.plane = 1024 * 512;
+  sdm_pa2_plan_t q;
+  int pa = sdm_pa2_check(&a, 1);
+  int pq = sdm_pa2_plan_for(&a, 256, 160 * 1024, &q);
+  printf("%d %d %d %d %d %d %d %d %d %s\n", sdm_gx_abi_version(), ok, bad, pl, plan.engine, pa, pq, q.slices_per_wave,
+         q.ctas, sdm_gx_strerror(bad));
+  return 0;
+}
+""")
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(B.lib_path())
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe), "-L", libdir,
+                    "-l:" + os.path.basename(B.lib_path()), f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True, timeout=120).stdout.split(maxsplit=9)
+    assert [int(v) for v in out[:9]] == [g.sdm_gx_abi_version(), B.SDM_GX_OK, B.SDM_GX_ERR_STRIDE, B.SDM_GX_OK,
+                                         B.SDM_GX_ENGINE_MFMA, B.SDM_GX_OK, B.SDM_GX_OK, 2, 1]
+    assert out[9].strip() == g.sdm_gx_strerror(B.SDM_GX_ERR_STRIDE)
+
 def test_strerror_covers_every_code():
     for code in range(0, -12, -1):
         assert g.sdm_gx_strerror(code) != "unknown status"

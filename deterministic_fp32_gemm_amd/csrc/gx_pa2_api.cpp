@@ -26,7 +26,9 @@ constexpr int kMinTile = 4;     // records per tile at least (4 measured 8% fast
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // LDS of a workgroup: token rows of its slices and beta, then, with staged outputs, a count and the outputs
-int64_t lds_base(const sdm_pa2_args_t* a, int32_t slices_per_wave) { return a->C * 16 * 32 * slices_per_wave + a->C * 4; }
+int64_t lds_base(const sdm_pa2_args_t* a, int32_t slices_per_wave) {
+    return a->C * 16 * 32 * slices_per_wave + a->C * 4;
+}
 int64_t lds_staged(const sdm_pa2_args_t* a, int32_t slices_per_wave) {
     const int64_t planes = (1 + (a->hd - 1) / 128 >= 2 && slices_per_wave == 2) ? 4 : 2;
     return 4 + planes * a->C * a->W * 4;
@@ -165,8 +167,9 @@ int device(int* dev, Dev* d) {
         c.known = true;
         c.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         c.num_cus = prop.multiProcessorCount;
-        c.lds_per_wg = static_cast<int>(prop.maxSharedMemoryPerMultiProcessor > 0 ? prop.maxSharedMemoryPerMultiProcessor
-                                                                                   : prop.sharedMemPerBlock);
+        c.lds_per_wg = static_cast<int>(prop.maxSharedMemoryPerMultiProcessor > 0
+                                             ? prop.maxSharedMemoryPerMultiProcessor
+                                             : prop.sharedMemPerBlock);
     }
     *d = c;
     return d->gfx950 ? SDM_GX_OK : SDM_GX_ERR_DEVICE;

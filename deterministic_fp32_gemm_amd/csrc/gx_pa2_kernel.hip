@@ -257,8 +257,10 @@ __device__ __forceinline__ void pa2_workgroup(const Pa2Args& a) {
     }
     asm volatile("" : "+v"(pq));                       // the ordinal's payload is examined here, not at its load
     int gw = 0;
-    if (a.ssr < 0)
-        gw = uniform(bp + static_cast<int>(__builtin_popcountll(__ballot(before_s && (pq & kFirst) && !(pq & kInvalid)))));
+    if (a.ssr < 0) {
+        const uint64_t before = __ballot(before_s && (pq & kFirst) && !(pq & kInvalid));
+        gw = uniform(bp + static_cast<int>(__builtin_popcountll(before)));
+    }
     const int64_t srow_base = a.ssr < 0 ? chunk * n : static_cast<int64_t>(a.ti) * a.ssr + static_cast<int64_t>(p) * n;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gdw = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};

@@ -272,6 +272,9 @@ int finish_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, const 
 // matrix cores also need C * ld_u * 4 < 2^31 (32-bit d_u offsets), else SDM_GX_ERR_LIMIT when forced.
 //  Matrix cores, direct-to-LDS slabs: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per
 //  work item of the 32-column MFMA), 3 LDS stages, 1 loader wavefront (1-3% faster than 4 stages; 6 or 8 slower).
+//  Where one workgroup per CU walks several items and hd is a multiple of 128: 64 x 128 items on four 32-column
+//  wavefronts (v_mfma_f32_32x32x1_2b_f32), 3 stages of 32 rows (2-3% faster warm and 3% cold than 16-column
+//  wavefronts on C = 64 and C = 128 chunks: half as many d_u accesses per item, whole 128-byte row segments).
 //  Work items of 64 or 128 rows (C <= 64 or not) by 64 columns; 32 columns when hd <= 32, or when 64-column items
 //  would leave CUs idle; 64 rows by 128 columns when C > 64 and hd is a multiple of 128 with items enough for every
 //  CU (2% faster than 128 x 64 at C = hd = 128). Two workgroups per CU when an item has fewer than 8 compute
@@ -324,6 +327,15 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, const Layout& lay, int engi
             st = complete_plan(&p, nchunks, C, hd, lds_limit);
             if (st == SDM_GX_OK && p.grid <= num_cus) {         // one workgroup per CU
                 if (items > p.grid) p.slab_rows = 32;           // walking several items: 32-row stages
+                if (items > p.grid && hd % 128 == 0) {          // streaming 64 x 128 items: 32-column wavefronts
+                    sdm_gx_plan_t q = p;
+                    q.mf_block = 32;
+                    q.mf_row_waves = 1;
+                    q.mf_col_waves = 4;
+                    q.mf_workgroups = num_cus;
+                    const int64_t items32 = nchunks * cdiv(C, 64) * (hd / 128);
+                    if (items32 > num_cus && complete_plan(&q, nchunks, C, hd, lds_limit) == SDM_GX_OK) p = q;
+                }
             } else {                                            // two per CU: streaming d_u stores
                 p.mf_stream_du = 1;
             }

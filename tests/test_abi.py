@@ -224,16 +224,25 @@ def test_plan_for_emits_supported_plans():
                 # or when 64-column items would leave CUs idle; 64 x 128 when C > 64 and hd is a multiple of 128 with
                 # items for every CU), 8 compute wavefronts per CU unless the items are many (4 or more per CU),
                 # 32-row stages when each CU holds one workgroup that walks several items
-                assert p.mf_block == 16 and p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1
+                assert p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1 and p.mf_du_at_end == 0
                 rw0 = 2 if C > 64 else 1
                 wide = hd > 32 and nchunks * cdiv(C, 64 * rw0) * cdiv(hd, 64) >= 256
                 long_rows = wide and C > 64 and hd % 128 == 0 and nchunks * cdiv(C, 64) * (hd // 128) >= 256
-                assert (p.mf_row_waves, p.mf_col_waves) == ((1, 8) if long_rows else (rw0, 4 if wide else 2))
-                assert p.mf_du_at_end == 0
-                items = nchunks * cdiv(cdiv(C, 64), p.mf_row_waves) * cdiv(hd, 16 * p.mf_col_waves)
-                two = p.mf_row_waves * p.mf_col_waves < 8 and items < 4 * 256
+                rw, cw = (1, 8) if long_rows else (rw0, 4 if wide else 2)
+                items = nchunks * cdiv(cdiv(C, 64), rw) * cdiv(hd, 16 * cw)
+                two = rw * cw < 8 and items < 4 * 256
+                grid16 = mfma_grid(items, 512 if two else 256)
+                # one workgroup per CU walking several items, hd a multiple of 128: 64 x 128 items on four 32-column
+                # wavefronts, 3 stages of 32 rows
+                items32 = nchunks * cdiv(C, 64) * (hd // 128)
+                if grid16 <= 256 and items > grid16 and hd % 128 == 0 and items32 > 256:
+                    assert (p.mf_block, p.mf_row_waves, p.mf_col_waves, p.slab_rows) == (32, 1, 4, 32)
+                    assert p.mf_workgroups == 256 and p.grid == mfma_grid(items32, 256) and p.mf_stream_du == 0
+                    assert p.lds_bytes == 16 * 3 * 32 * (16 + 8 * 4)
+                    continue
+                assert p.mf_block == 16 and (p.mf_row_waves, p.mf_col_waves) == (rw, cw)
                 assert p.mf_workgroups == (512 if two else 256)
-                assert p.grid == mfma_grid(items, p.mf_workgroups)
+                assert p.grid == grid16
                 assert p.slab_rows == (32 if p.grid <= 256 and items > p.grid else 16)
                 assert p.mf_stream_du == (0 if p.grid <= 256 else 1)
                 assert p.lds_bytes == 16 * 3 * p.slab_rows * (16 * p.mf_row_waves + 4 * p.mf_col_waves)
@@ -297,7 +306,7 @@ MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs
                   if (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
                  [(2, 4, 4, 2, 4, 1, 32, 16), (1, 4, 4, 2, 4, 1, 32, 16)] + \
                  [(rw, cw, s, 0, lw, 0, 32, 16) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
-                 [(2, 4, 4, 0, 1, 1, 32, 16)] + \
+                 [(2, 4, 4, 0, 1, 1, 32, 16), (1, 4, 3, 0, 1, 0, 32, 32)] + \
                  [(rw, cw, s, 0, lw, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
                   for s, lw, j in ((3, 1, 16), (8, 2, 16), (3, 1, 32))]
 # and, for each 16-column (3 stages, 1 loader) instance, twins for rows off a 16-byte boundary, picked at launch
@@ -348,16 +357,22 @@ def test_mfma_direct_to_lds_rejects_missing_instances():
 def test_plan_resolves_the_layout():
     """The planner takes the row strides and the placement of x and d_dv, and reports the instance that a launch with
     that layout runs (unaligned-row twins, or the register ring where the strides rule out direct-to-LDS slabs)."""
-    # workload 5's layout: ld 260, d_u and d_dv at +4 bytes, x aligned: d_dv rows by 4-byte DMA
+    # workload 5's layout: ld 260, d_u and d_dv at +4 bytes, x aligned: 64 x 128 items of 32-column wavefronts with
+    # 32-row stages, which have no 4-byte-DMA twin: d_dv rows from the 16-byte boundary below (33 groups per row)
     p = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=0, dv_mod16=4)
-    assert (p.engine, p.mf_reg_slabs, p.mf_block, p.mf_aln) == (g.SDM_GX_ENGINE_MFMA, 0, 16, 4)
-    assert p.lds_bytes == 16 * 3 * p.slab_rows * 16 + 4 * 3 * p.slab_rows * 16 * p.mf_col_waves
+    assert (p.engine, p.mf_reg_slabs, p.mf_block, p.mf_col_waves, p.slab_rows, p.mf_aln) == \
+        (g.SDM_GX_ENGINE_MFMA, 0, 32, 4, 32, 2)
+    assert p.lds_bytes == 16 * 3 * (32 * 16 + 64 * cdiv(32 * 33, 64))
     # x off the boundary too: both from the 16-byte boundary below (one more group per LDS row)
     q = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=8, dv_mod16=4)
-    assert (q.mf_reg_slabs, q.mf_aln) == (0, 3) and q.lds_bytes > p.lds_bytes
-    # 64 x 128 items with 32-row stages have no 4-byte-DMA twin: from the boundary below
+    assert (q.mf_reg_slabs, q.mf_block, q.mf_aln) == (0, 32, 3) and q.lds_bytes > p.lds_bytes
+    # 16-column wavefronts (hd not a multiple of 128): d_dv rows by 4-byte DMA
+    t = g.sdm_gx_plan_for(1024, 64, 192, ld_u=196, ld_dv=196, x_mod16=0, dv_mod16=4)
+    assert (t.mf_reg_slabs, t.mf_block, t.mf_aln) == (0, 16, 4)
+    assert t.lds_bytes == 16 * 3 * t.slab_rows * 16 + 4 * 3 * t.slab_rows * 16 * t.mf_col_waves
+    # workload 4's shape with d_dv off the boundary: the 32-column 64 x 128 items, from the boundary below
     r = g.sdm_gx_plan_for(512, 128, 128, x_mod16=0, dv_mod16=12)
-    assert (r.mf_row_waves, r.mf_col_waves, r.slab_rows, r.mf_aln) == (1, 8, 32, 2)
+    assert (r.mf_row_waves, r.mf_col_waves, r.mf_block, r.slab_rows, r.mf_aln) == (1, 4, 32, 32, 2)
     # a row stride that is not a multiple of 4: the register ring (hd <= 128), or the vector ALUs (hd > 128)
     s_ = g.sdm_gx_plan_for(256, 64, 128, ld_u=131, ld_dv=131)
     assert (s_.engine, s_.mf_reg_slabs, s_.mf_block, s_.mf_aln) == (g.SDM_GX_ENGINE_MFMA, 4, 32, 0)
@@ -375,7 +390,12 @@ def test_plan_complete_resolves_the_layout():
     assert g.sdm_gx_plan_complete(p, 64, 64, 128).mf_aln == 0
     p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 16, 16), 64, 64, 128, dv_mod16=8)
     assert (p.mf_reg_slabs, p.mf_aln, p.mf_col_waves) == (0, 4, 4)
-    # 32-column direct-to-LDS instances have no twins: the register ring, same tile
+    # the 32-column 64 x 128 instance with 32-row stages has twins (d_dv rows, and x rows too, from the boundary below)
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 32, 32), 64, 64, 256, dv_mod16=8)
+    assert (p.mf_reg_slabs, p.mf_block, p.mf_aln) == (0, 32, 2)
+    p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 4, 3, 0, 1, 0, 0, 32, 32), 64, 64, 256, x_mod16=4)
+    assert (p.mf_reg_slabs, p.mf_block, p.mf_aln) == (0, 32, 3)
+    # the other 32-column direct-to-LDS instances have no twins: the register ring, same tile
     p = g.sdm_gx_plan_complete(g.make_mfma_plan(1, 2, 4, 0, 1, 0, 0, 32, 16), 64, 64, 128, x_mod16=4)
     assert (p.mf_reg_slabs, p.mf_stages, p.mf_loader_waves, p.mf_block, p.mf_col_waves, p.mf_aln) == \
         (2, 4, 4, 32, 2, 0)

@@ -273,8 +273,9 @@ int finish_plan(sdm_gx_plan_t* p, int64_t nchunks, int64_t C, int64_t hd, const 
 //  Matrix cores, direct-to-LDS slabs: 16-column wavefronts (v_mfma_f32_16x16x1_4b_f32: half the chain latency per
 //  work item of the 32-column MFMA), 3 LDS stages, 1 loader wavefront (1-3% faster than 4 stages; 6 or 8 slower).
 //  Where one workgroup per CU walks several items and hd is a multiple of 128: 64 x 128 items on four 32-column
-//  wavefronts (v_mfma_f32_32x32x1_2b_f32), 3 stages of 32 rows (2-3% faster warm and 3% cold than 16-column
-//  wavefronts on C = 64 and C = 128 chunks: half as many d_u accesses per item, whole 128-byte row segments).
+//  wavefronts (v_mfma_f32_32x32x1_2b_f32), 3 stages of 32 rows and 2 loader wavefronts (1 when x rows are off a
+//  16-byte boundary, whose twin needs the extra group per row): half as many d_u accesses per item, in 128-byte row
+//  segments; up to 3% faster warm and cold than 16-column wavefronts on C = 64 and C = 128 chunks.
 //  Work items of 64 or 128 rows (C <= 64 or not) by 64 columns; 32 columns when hd <= 32, or when 64-column items
 //  would leave CUs idle; 64 rows by 128 columns when C > 64 and hd is a multiple of 128 with items enough for every
 //  CU (2% faster than 128 x 64 at C = hd = 128). Two workgroups per CU when an item has fewer than 8 compute
@@ -333,6 +334,7 @@ int plan_for(int64_t nchunks, int64_t C, int64_t hd, const Layout& lay, int engi
                     q.mf_row_waves = 1;
                     q.mf_col_waves = 4;
                     q.mf_workgroups = num_cus;
+                    q.mf_loader_waves = lay.x_mod16 == 0 ? 2 : 1;   // 2: d_dv rows by 4-byte DMA when unaligned
                     const int64_t items32 = nchunks * cdiv(C, 64) * (hd / 128);
                     if (items32 > num_cus && complete_plan(&q, nchunks, C, hd, lds_limit) == SDM_GX_OK) p = q;
                 }

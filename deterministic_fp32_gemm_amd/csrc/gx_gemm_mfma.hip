@@ -583,8 +583,9 @@ __global__ __launch_bounds__(64 * (RW * QW + LW), MINW) void gx_mfma_dma_kernel(
 
 // Direct-to-LDS instances (reg_slabs = 0). 32-column tiles: S = 4 stages of 16 chain rows and 1 loader wavefront,
 // and S = 8 and 2 loader wavefronts; the 128 x 128 tile also reading d_u at the item's end, built for two
-// workgroups per CU; 64 x 128 tiles (1 x 4 wavefronts) with S = 3 stages of 32 rows, also for rows off a 16-byte
-// boundary (ALN 2 and 3). 16-column tiles: S = 3 stages of 16 or 32 chain rows and 1 loader wavefront (also for rows off
+// workgroups per CU; 64 x 128 tiles (1 x 4 wavefronts) with S = 3 stages of 32 rows: with 2 loader wavefronts
+// (also with d_dv rows by 4-byte DMA, ALN 4), and with 1 (also with rows from the 16-byte boundary below, ALN 2 and 3,
+// for unaligned x). 16-column tiles: S = 3 stages of 16 or 32 chain rows and 1 loader wavefront (also for rows off
 // a 16-byte boundary, chosen at launch from the pointers: ALN 4 d_dv rows by 4-byte DMA, or ALN 2 from the boundary
 // below where 4-byte DMA would exceed the vmcnt range (64 x 128 tiles with 32-row stages); ALN 3 x rows too), and
 // S = 8 of 16 rows with 2 loader wavefronts.
@@ -607,6 +608,7 @@ const MfmaEntry kMfmaTable[] = {
     SDM_GX_MD2(1, 1, 32) SDM_GX_MD2(1, 2, 32) SDM_GX_MD2(1, 4, 32) SDM_GX_MD2(1, 8, 32) SDM_GX_MD2(2, 1, 32)
     SDM_GX_MD2(2, 2, 32) SDM_GX_MD2(2, 4, 32) SDM_GX_MD(2, 4, 4, 1, 1, 5, 32, 16)
     SDM_GX_MD(1, 4, 3, 1, 0, 1, 32, 32) SDM_GX_MD_A(1, 4, 3, 1, 0, 1, 32, 32, 2) SDM_GX_MD_A(1, 4, 3, 1, 0, 1, 32, 32, 3)
+    SDM_GX_MD(1, 4, 3, 2, 0, 1, 32, 32) SDM_GX_MD_A(1, 4, 3, 2, 0, 1, 32, 32, 4)
     SDM_GX_MD3(1, 2) SDM_GX_MD3(1, 4) SDM_GX_MD3(1, 8) SDM_GX_MD3(2, 2) SDM_GX_MD3(2, 4)
     SDM_GX_MD4(1, 2) SDM_GX_MD4(1, 4) SDM_GX_MD4(2, 2) SDM_GX_MD4(2, 4) SDM_GX_MD_A(1, 8, 3, 1, 0, 1, 16, 16, 4)
     SDM_GX_MF_RL(1, 1) SDM_GX_MF_RL(1, 2) SDM_GX_MF_RL(1, 4)

@@ -224,7 +224,7 @@ def test_plan_for_emits_supported_plans():
                 # or when 64-column items would leave CUs idle; 64 x 128 when C > 64 and hd is a multiple of 128 with
                 # items for every CU), 8 compute wavefronts per CU unless the items are many (4 or more per CU),
                 # 32-row stages when each CU holds one workgroup that walks several items
-                assert p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_loader_waves == 1 and p.mf_du_at_end == 0
+                assert p.mf_reg_slabs == 0 and p.mf_stages == 3 and p.mf_du_at_end == 0
                 rw0 = 2 if C > 64 else 1
                 wide = hd > 32 and nchunks * cdiv(C, 64 * rw0) * cdiv(hd, 64) >= 256
                 long_rows = wide and C > 64 and hd % 128 == 0 and nchunks * cdiv(C, 64) * (hd // 128) >= 256
@@ -236,11 +236,11 @@ def test_plan_for_emits_supported_plans():
                 # wavefronts, 3 stages of 32 rows
                 items32 = nchunks * cdiv(C, 64) * (hd // 128)
                 if grid16 <= 256 and items > grid16 and hd % 128 == 0 and items32 > 256:
-                    assert (p.mf_block, p.mf_row_waves, p.mf_col_waves, p.slab_rows) == (32, 1, 4, 32)
+                    assert (p.mf_block, p.mf_row_waves, p.mf_col_waves, p.slab_rows, p.mf_loader_waves) == (32, 1, 4, 32, 2)
                     assert p.mf_workgroups == 256 and p.grid == mfma_grid(items32, 256) and p.mf_stream_du == 0
                     assert p.lds_bytes == 16 * 3 * 32 * (16 + 8 * 4)
                     continue
-                assert p.mf_block == 16 and (p.mf_row_waves, p.mf_col_waves) == (rw, cw)
+                assert p.mf_block == 16 and (p.mf_row_waves, p.mf_col_waves) == (rw, cw) and p.mf_loader_waves == 1
                 assert p.mf_workgroups == (512 if two else 256)
                 assert p.grid == grid16
                 assert p.slab_rows == (32 if p.grid <= 256 and items > p.grid else 16)
@@ -306,7 +306,7 @@ MFMA_INSTANCES = [(rw, cw, 4, rs, lw, 0, 32, 16) for rw, cw in MFMA_TILES for rs
                   if (rw, cw, rs, lw) not in ((1, 8, 4, 2), (2, 4, 4, 2))] + \
                  [(2, 4, 4, 2, 4, 1, 32, 16), (1, 4, 4, 2, 4, 1, 32, 16)] + \
                  [(rw, cw, s, 0, lw, 0, 32, 16) for rw, cw in MFMA_TILES for s, lw in ((4, 1), (8, 2))] + \
-                 [(2, 4, 4, 0, 1, 1, 32, 16), (1, 4, 3, 0, 1, 0, 32, 32)] + \
+                 [(2, 4, 4, 0, 1, 1, 32, 16), (1, 4, 3, 0, 1, 0, 32, 32), (1, 4, 3, 0, 2, 0, 32, 32)] + \
                  [(rw, cw, s, 0, lw, 0, 16, j) for rw, cw in ((1, 2), (1, 4), (1, 8), (2, 2), (2, 4))
                   for s, lw, j in ((3, 1, 16), (8, 2, 16), (3, 1, 32))]
 # and, for each 16-column (3 stages, 1 loader) instance, twins for rows off a 16-byte boundary, picked at launch
@@ -358,21 +358,21 @@ def test_plan_resolves_the_layout():
     """The planner takes the row strides and the placement of x and d_dv, and reports the instance that a launch with
     that layout runs (unaligned-row twins, or the register ring where the strides rule out direct-to-LDS slabs)."""
     # workload 5's layout: ld 260, d_u and d_dv at +4 bytes, x aligned: 64 x 128 items of 32-column wavefronts with
-    # 32-row stages, which have no 4-byte-DMA twin: d_dv rows from the 16-byte boundary below (33 groups per row)
+    # 32-row stages and 2 loader wavefronts, d_dv rows by 4-byte DMA (LDS rows exactly the item's 128 columns)
     p = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=0, dv_mod16=4)
-    assert (p.engine, p.mf_reg_slabs, p.mf_block, p.mf_col_waves, p.slab_rows, p.mf_aln) == \
-        (g.SDM_GX_ENGINE_MFMA, 0, 32, 4, 32, 2)
-    assert p.lds_bytes == 16 * 3 * (32 * 16 + 64 * cdiv(32 * 33, 64))
-    # x off the boundary too: both from the 16-byte boundary below (one more group per LDS row)
+    assert (p.engine, p.mf_reg_slabs, p.mf_block, p.mf_col_waves, p.slab_rows, p.mf_loader_waves, p.mf_aln) == \
+        (g.SDM_GX_ENGINE_MFMA, 0, 32, 4, 32, 2, 4)
+    assert p.lds_bytes == 16 * 3 * (32 * 16 + 32 * 32)
+    # x off the boundary too: 1 loader wavefront, both from the 16-byte boundary below (one more group per LDS row)
     q = g.sdm_gx_plan_for(1024, 64, 256, ld_u=260, ld_dv=260, x_mod16=8, dv_mod16=4)
-    assert (q.mf_reg_slabs, q.mf_block, q.mf_aln) == (0, 32, 3) and q.lds_bytes > p.lds_bytes
+    assert (q.mf_reg_slabs, q.mf_block, q.mf_loader_waves, q.mf_aln) == (0, 32, 1, 3) and q.lds_bytes > p.lds_bytes
     # 16-column wavefronts (hd not a multiple of 128): d_dv rows by 4-byte DMA
     t = g.sdm_gx_plan_for(1024, 64, 192, ld_u=196, ld_dv=196, x_mod16=0, dv_mod16=4)
     assert (t.mf_reg_slabs, t.mf_block, t.mf_aln) == (0, 16, 4)
     assert t.lds_bytes == 16 * 3 * t.slab_rows * 16 + 4 * 3 * t.slab_rows * 16 * t.mf_col_waves
-    # workload 4's shape with d_dv off the boundary: the 32-column 64 x 128 items, from the boundary below
+    # workload 4's shape with d_dv off the boundary: the 32-column 64 x 128 items, d_dv rows by 4-byte DMA
     r = g.sdm_gx_plan_for(512, 128, 128, x_mod16=0, dv_mod16=12)
-    assert (r.mf_row_waves, r.mf_col_waves, r.mf_block, r.slab_rows, r.mf_aln) == (1, 4, 32, 32, 2)
+    assert (r.mf_row_waves, r.mf_col_waves, r.mf_block, r.slab_rows, r.mf_aln) == (1, 4, 32, 32, 4)
     # a row stride that is not a multiple of 4: the register ring (hd <= 128), or the vector ALUs (hd > 128)
     s_ = g.sdm_gx_plan_for(256, 64, 128, ld_u=131, ld_dv=131)
     assert (s_.engine, s_.mf_reg_slabs, s_.mf_block, s_.mf_aln) == (g.SDM_GX_ENGINE_MFMA, 4, 32, 0)

@@ -57,7 +57,7 @@ def test_every_kernel_instance_has_no_scratch_and_no_spills(tmp_path):
     names = [n for n, _ in found]
     assert sum("gx_chain_kernel" in n for n in names) == 134
     assert sum("gx_mfma_kernel" in n for n in names) == 28
-    assert sum("gx_mfma_dma_kernel" in n for n in names) == 62
+    assert sum("gx_mfma_dma_kernel" in n for n in names) == 64
     assert sum("gx_pa2_kernel" in n for n in names) == 6
     assert sum("gx_pa2_staged_kernel" in n for n in names) == 6
     for name, f in found:

@@ -181,6 +181,32 @@ def test_every_plan_is_bit_identical(C, hd, ld, res):
     assert n > 100
 
 
+
+@pytest.mark.parametrize("res_v", [4, 8, 12])
+def test_unaligned_dv_rows_with_aligned_x(res_v):
+    """x on a 16-byte boundary and d_dv (and d_u) off it, as in workload 5: the instances that move d_dv rows by 4-byte
+    DMA (the 64 x 128 items of 32-column wavefronts with two loader wavefronts, the 16-column ones) and those that
+    read them from the boundary below, each against the oracle; ragged C and hd tails, several items per
+    workgroup."""
+    N, P, C, hd, ld = 12, 4, 60, 250, 252
+    x, dv, du = inputs.shape_inputs(N, C, hd, ld, "hazard_cancel", seed=res_v)
+    case = DeviceCase(x, dv, du, hd, res_u=res_v, res_v=res_v, res_x=0)
+    want = expected(x, dv, du, hd, 0, N)
+    plans = [None, g.make_mfma_plan(1, 4, 3, 0, 2, 3, 0, 32, 32), g.make_mfma_plan(1, 4, 3, 0, 1, 3, 0, 32, 32),
+             g.make_mfma_plan(1, 4, 3, 0, 1, 3, 0, 16, 32), g.make_mfma_plan(1, 4, 3, 0, 1, 3, 0, 16, 16),
+             g.make_mfma_plan(1, 8, 3, 0, 1, 3, 0, 16, 32)]
+    seen = set()
+    for plan in plans:
+        case.reset()
+        say(f"unaligned d_dv +{res_v}: plan {plan}")
+        got = run_steps(case, P, 0, N // P, g.SDM_GX_STEPS_FUSED, plan)
+        assert_matches(got, want, du, hd, f"d_dv +{res_v} plan {plan}")
+        geom = g.sdm_gx_plan_complete(type(plan).from_buffer_copy(plan), N, C, hd, ld_u=ld, ld_dv=ld,
+                                      dv_mod16=res_v % 16) if plan is not None else None
+        if geom is not None:
+            seen.add((geom.mf_block, geom.mf_loader_waves, geom.mf_aln))
+    assert (32, 2, 4) in seen and (32, 1, 2) in seen and (16, 1, 4) in seen
+
 @pytest.mark.parametrize("C", [1, 5, 16, 17, 20, 33, 64, 65, 128, 130])
 def test_signed_zero_through_padded_steps(C):
     """Products that round to -0 keep the accumulator at -0, and -0 + -0 stays -0 in d_u. The matrix-core engine

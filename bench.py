@@ -481,7 +481,8 @@ def main():
     if not args.no_phase_a:
         for key in ("a3", "a5"):
             pb = Pa2Bench(g, torch, key)
-            e = {"description": pb.w.description, "plan": pb.plan.as_dict(), "kernel": "gx_pa2_kernel",
+            e = {"description": pb.w.description, "plan": pb.plan.as_dict(),
+                 "kernel": "gx_pa2_staged_kernel" if pb.plan.stage_out else "gx_pa2_kernel",
                  "algorithmic_bytes_per_pass": pb.bytes_pass, "algorithmic_flops_per_pass": pb.flops_pass}
             pb.one_pass()
             got = pb.result()

@@ -78,7 +78,7 @@ class sdm_pa2_args_t(ctypes.Structure):
 class sdm_pa2_plan_t(ctypes.Structure):
     _fields_ = [("slices_per_wave", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("tile_len", ctypes.c_int32),
                 ("ctas", ctypes.c_int32), ("npair", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("grid", ctypes.c_int64)]
+                ("stage_out", ctypes.c_int32), ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -6,7 +6,7 @@
 
 namespace sdm_gx {
 
-// One launch = one step ti: grid P * npair * ctas workgroups (cta fastest, then slice pair, then chunk).
+// One launch = one step ti: grid P * npair * ctas workgroups (slice pair fastest, then chunk, then cta).
 struct Pa2Args {
     float* grad;            // [slots][hd]
     float* bank;            // [slots][hd]

@@ -39,7 +39,7 @@ int64_t lds_staged(const sdm_pa2_args_t* a, int32_t slices_per_wave) {
 // record and plane (with the 80-SGPR instance, 3.7% off a5's step).
 bool stage_outputs(const sdm_pa2_args_t* a, const sdm_pa2_plan_t& p) {
     const int64_t base = lds_base(a, p.slices_per_wave), staged = lds_staged(a, p.slices_per_wave);
-    return p.ctas == 1 && 4 * staged <= base && p.lds_bytes == base + staged;
+    return p.stage_out == 1 && p.ctas == 1 && 4 * staged <= base && p.lds_bytes == base + staged;
 }
 
 struct Extent {
@@ -108,10 +108,12 @@ int complete(const sdm_pa2_args_t* a, int lds_limit, sdm_pa2_plan_t* p) {
     const int64_t base = lds_base(a, p->slices_per_wave), staged = lds_staged(a, p->slices_per_wave);
     if (lds_limit > 0 && base > lds_limit) {
         p->lds_bytes = static_cast<int32_t>(base);
+        p->stage_out = 0;
         return SDM_GX_ERR_LIMIT;
     }
     const bool stage = p->ctas == 1 && 4 * staged <= base && (lds_limit <= 0 || base + staged <= lds_limit);
     p->lds_bytes = static_cast<int32_t>(stage ? base + staged : base);
+    p->stage_out = stage ? 1 : 0;
     const int64_t grid = a->P * p->npair * p->ctas;
     if (grid >= (int64_t(1) << 31)) return SDM_GX_ERR_LIMIT;
     p->grid = grid;

@@ -155,8 +155,9 @@ __device__ __forceinline__ void pa2_workgroup(const Pa2Args& a) {
     const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
     const int half = lane >> 5, hl = lane & 31;
     int b = static_cast<int>(blockIdx.x);
-    const int cta = b % a.ctas;
-    b /= a.ctas;
+    const int units = a.P * a.npair;                   // (chunk, slice pair) units of the step, cta slowest:
+    const int cta = b / units;                         // workgroups are dealt to the 8 XCDs round-robin, so when
+    b -= cta * units;                                  // units is a multiple of 8 a chunk's workgroups share one L2
     const int sp = b % a.npair;
     const int p = b / a.npair;
     const int C = a.C, W = a.W, n = a.n, hd = a.hd;

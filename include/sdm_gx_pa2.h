@@ -73,9 +73,9 @@ typedef struct sdm_pa2_args {
 /* How a step is launched (never changes results): slices_per_wave 2 puts two slices in one wavefront (lanes 0-31 and
  * 32-63; the planner's choice when nsl >= 2 and C <= 128), 1 one slice; waves_per_wg 4, 8 or 16 wavefronts per
  * workgroup, which stages a chunk's token rows once; tile_len records per wavefront tile (tiles move back to group
- * starts). Outputs: ctas, npair (slice groups), grid, lds_bytes. When one workgroup covers a chunk (ctas == 1) and
- * the chunk's outputs add at most a quarter to its LDS, it gathers them in LDS and writes each output plane of the
- * chunk in one contiguous run; lds_bytes then includes them. */
+ * starts). Outputs: ctas, npair (slice groups), grid, lds_bytes, stage_out. When one workgroup covers a chunk (ctas
+ * == 1) and the chunk's outputs add at most a quarter to its LDS, it gathers them in LDS and writes each output plane
+ * of the chunk in one contiguous run (stage_out 1, the kernel gx_pa2_staged_kernel); lds_bytes then includes them. */
 typedef struct sdm_pa2_plan {
     int32_t slices_per_wave;
     int32_t waves_per_wg;
@@ -83,6 +83,7 @@ typedef struct sdm_pa2_plan {
     int32_t ctas;
     int32_t npair;
     int32_t lds_bytes;
+    int32_t stage_out;
     int64_t grid;
 } sdm_pa2_plan_t;
 

@@ -98,7 +98,7 @@ def test_planner_one_slice_small_chunks():
     st, p = plan(args())
     assert st == B.SDM_GX_OK
     assert (p.slices_per_wave, p.waves_per_wg, p.tile_len, p.ctas, p.npair) == (1, 16, 4, 8, 1)
-    assert p.grid == 32 * 8 and p.lds_bytes == 64 * 16 * 32 + 64 * 4
+    assert p.grid == 32 * 8 and p.lds_bytes == 64 * 16 * 32 + 64 * 4 and p.stage_out == 0
 
 
 def test_planner_two_slices():
@@ -108,8 +108,7 @@ def test_planner_two_slices():
     assert st == B.SDM_GX_OK
     assert (p.slices_per_wave, p.waves_per_wg, p.tile_len, p.ctas, p.npair) == (2, 16, 32, 1, 1)
     # one workgroup per chunk: its four output planes (2 slices x 2 outputs x 512 records) and a count go to LDS too
-    assert p.grid == 512 and p.lds_bytes == 64 * 16 * 64 + 64 * 4 + 4 + 4 * 512 * 4
-
+    assert p.grid == 512 and p.lds_bytes == 64 * 16 * 64 + 64 * 4 + 4 + 4 * 512 * 4 and p.stage_out == 1
 
 
 def test_planner_stages_outputs_only_when_cheap():
@@ -117,11 +116,12 @@ def test_planner_stages_outputs_only_when_cheap():
     total fits the limit."""
     a = args(P=512, N=1024, hd=256, ld_u=260, slots=1 << 17, ssr=512 * 512)
     st, p = plan(a, lds=70000)                            # 73988 bytes with the outputs: left out
-    assert st == B.SDM_GX_OK and p.ctas == 1 and p.lds_bytes == 64 * 16 * 64 + 64 * 4
+    assert st == B.SDM_GX_OK and p.ctas == 1 and p.lds_bytes == 64 * 16 * 64 + 64 * 4 and p.stage_out == 0
     st, p = plan(args(P=512, N=1024, C=4, W=256, hd=16, slots=1 << 17))   # outputs 4x the token rows: left out
-    assert st == B.SDM_GX_OK and p.ctas == 1 and p.lds_bytes == 4 * 16 * 32 + 4 * 4
+    assert st == B.SDM_GX_OK and p.ctas == 1 and p.lds_bytes == 4 * 16 * 32 + 4 * 4 and p.stage_out == 0
     st, p = plan(args(), lds=0)                           # 8 workgroups per chunk: never staged
-    assert st == B.SDM_GX_OK and p.ctas == 8 and p.lds_bytes == 64 * 16 * 32 + 64 * 4
+    assert st == B.SDM_GX_OK and p.ctas == 8 and p.lds_bytes == 64 * 16 * 32 + 64 * 4 and p.stage_out == 0
+
 
 def test_planner_three_slices_and_wide_tokens():
     st, p = plan(args(P=4, N=8, hd=300))                  # three slices: a pair and a single

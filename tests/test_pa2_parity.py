@@ -144,7 +144,6 @@ def test_every_plan_gives_the_same_bits():
     assert n == 42
 
 
-
 @pytest.mark.parametrize("mode", ["forward", "reverse"])
 def test_gathered_outputs_over_steps(mode):
     """Outputs gathered in LDS (one workgroup per chunk, two slices, d_u rows off a 16-byte boundary), over three
@@ -158,6 +157,7 @@ def test_gathered_outputs_over_steps(mode):
     order = range(w.T) if mode == "forward" else reversed(range(w.T))
     g.sdm_pa2_steps(c.args, 0, w.T, g.SDM_GX_STEPS_FORWARD if mode == "forward" else g.SDM_GX_STEPS_REVERSE, plan)
     assert_same(c.result(), c.expect(order), f"gathered outputs {mode}")
+
 
 def test_planner_plans():
     for key, sg in (("a1", 1), ("a3", 1), ("a5", 2)):
